@@ -1,0 +1,117 @@
+"""Seeded synthetic inputs for exact attention.
+
+This module only draws random numbers and names workloads. It holds none of
+the attention arithmetic, so that both the HIP path (through its tests and the
+benchmark) and the CPU oracle can take their inputs from it without sharing
+any of the method's code.
+
+Every tensor is [B, H, N, d], contiguous, head dimension fastest, which is the
+per-(batch, head) row layout that the pages index as Q[batch, head, rows, :]
+(page "FlashAttention算子优化", §2 pseudocode; page "Attention 算子优化:从物化
+N×N 矩阵到 FlashAttention 与 PagedAttention", §一).
+
+Values are i.i.d. standard normal, which is the distribution the AIInfra
+FlashAttention note (dpshk.com, §3.1) prescribes for the random-comparison
+layer of its verification matrix. For 16-bit workloads the fp32 draws are
+rounded to bfloat16 with round-to-nearest-even (torch's ``.to(bfloat16)``);
+the very same bits are what the GPU path and the oracle both consume.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "draw_seqlens", "workload"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One named synthetic workload.
+
+    ``seqlen_range`` (inclusive) switches on a padded variable-length batch:
+    one length per sequence, drawn uniformly from the range after the tensors.
+    ``with_grad`` also draws the upstream gradient dO.
+    """
+
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str  # "f32" or "bf16"
+    causal: bool
+    seed: int
+    seqlen_range: Optional[tuple[int, int]] = None
+    with_grad: bool = False
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(self.d) ** 0.5
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+
+# The five workloads of this project: shapes, masks and precisions.
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("single_head_f32_n256_d64", 1, 1, 256, 64, "f32", False, 1001,
+                 description="single head, non-causal, fp32, N=256, d=64"),
+        Workload("mha_bf16_b4_h16_n2048_d64", 4, 16, 2048, 64, "bf16", False, 1002,
+                 description="batched MHA forward, non-causal, bf16, B=4 H=16 N=2048 d=64"),
+        Workload("causal_bf16_b2_h32_n4096_d128", 2, 32, 4096, 128, "bf16", True, 1003,
+                 description="batched MHA forward, causal, bf16, B=2 H=32 N=4096 d=128"),
+        Workload("varlen_bf16_b8_h16_n2048_d128", 8, 16, 2048, 128, "bf16", False, 1004,
+                 seqlen_range=(512, 2048),
+                 description="padded variable-length batch, key-padding mask, bf16, "
+                             "8 sequences of length U{512..2048} padded to 2048, H=16 d=128"),
+        Workload("causal_fwdbwd_bf16_b2_h16_n8192_d128", 2, 16, 8192, 128, "bf16", True, 1005,
+                 with_grad=True,
+                 description="forward + recompute backward, causal, bf16, B=2 H=16 N=8192 d=128"),
+    ]
+}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def draw_seqlens(gen: torch.Generator, B: int, lo: int, hi: int) -> torch.Tensor:
+    """Per-sequence lengths, int32 uniform on the inclusive range [lo, hi]."""
+    return torch.randint(lo, hi + 1, (B,), generator=gen, dtype=torch.int64).to(torch.int32)
+
+
+def make_inputs(B: int, H: int, N: int, d: int, dtype: torch.dtype = torch.bfloat16,
+                seed: int = 0, with_grad: bool = False,
+                seqlen_range: Optional[tuple[int, int]] = None,
+                std: float = 1.0) -> dict:
+    """Draw Q, K, V (and dO, then seqlens) on the CPU from one seeded generator.
+
+    The draw order is fixed (Q, K, V, dO, seqlens) so a workload is the same
+    bits on every machine. Returns CPU tensors in ``dtype``; ``seqlens`` is an
+    int32 [B] tensor or None.
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    shape = (B, H, N, d)
+
+    def draw() -> torch.Tensor:
+        x = torch.randn(shape, generator=gen, dtype=torch.float32)
+        if std != 1.0:
+            x = x * std
+        return x.to(dtype).contiguous()
+
+    out = {"q": draw(), "k": draw(), "v": draw()}
+    out["do"] = draw() if with_grad else None
+    out["seqlens"] = (draw_seqlens(gen, B, *seqlen_range)
+                      if seqlen_range is not None else None)
+    return out
+
+
+def make_workload_inputs(w: Workload) -> dict:
+    return make_inputs(w.B, w.H, w.N, w.d, w.torch_dtype, w.seed, w.with_grad, w.seqlen_range)
