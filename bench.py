@@ -1,0 +1,141 @@
+#!/usr/bin/env python3
+"""Benchmark: attention forward TFLOPS at B=2, H=32, N=4096, d=128, causal, bf16.
+
+One step is one forward pass (one kernel launch) over the whole batch, with
+Q/K/V resident in device memory before the timed region. FLOPs are counted as
+4*B*H*N^2*d, halved for the causal mask (only the lower triangle is work).
+Prints ONE JSON line.
+
+Timing follows the method of the AIInfra FlashAttention note (dpshk.com,
+§3.2): warm-up launches first, device synchronisation on both sides of the
+timed region, per-launch HIP events recorded on the stream the kernel runs
+on, median reported alongside the mean.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+WORKLOAD = "causal_bf16_b2_h32_n4096_d128"
+METRIC = "attention fwd TFLOPS (and % of bf16 MFMA peak) at B=2,H=32,N=4096,d=128 causal"
+
+
+def fwd_flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def cpu_baseline(x, w, budget_s: float):
+    """Time the fp64 CPU oracle on a bounded sample of the same workload: whole
+    (b, h) heads, one after another, until about ``budget_s`` seconds are spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        oracle.attn_ref_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    flops = fwd_flops(1, 1, w.N, w.d, w.causal) * done
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle (three-pass softmax, S and P materialised) on {done} of "
+                      f"{len(heads)} (b,h) heads of {WORKLOAD}; {el:.1f} s; host cpu_count="
+                      f"{os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle time for the CPU baseline (0 disables it)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_24_amd as ea
+    from attn_inputs import WORKLOADS, make_workload_inputs
+
+    w = WORKLOADS[WORKLOAD]
+    x = make_workload_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ea.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms per launch
+    mean_ms = sum(per) / len(per)
+    median_ms = per[len(per) // 2]
+    ms_per_step = wall * 1e3 / args.steps
+    flops = fwd_flops(w.B, w.H, w.N, w.d, w.causal)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "kernel_ms": {"mean": round(mean_ms, 4), "median": round(median_ms, 4),
+                      "p90": round(per[int(0.9 * (len(per) - 1))], 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "fwd_bf16_kernel<128, causal>",
+                     "algorithmic": "4*B*H*N^2*d/2 FLOP per launch"},
+    }
+    if args.cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(x, w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+"""Exact scaled dot-product attention for AMD MI355X (gfx950).
+
+Thin ctypes binding over the C-ABI library ``lib/libattn.so`` (see
+``include/attn.h``). This module only marshals arguments: it checks tensor
+shapes and types, allocates outputs with PyTorch (device memory is PyTorch's
+job here) and passes raw device pointers and the current HIP stream to the
+library. Every step of the computation runs in the library's HIP kernels;
+there is no fallback path — if the library is missing, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import pathlib
+from typing import Optional
+
+__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string",
+           "AttnError", "lib", "LIB_PATH", "DTYPE_F32", "DTYPE_BF16", "EXPORTED_SYMBOLS"]
+
+LIB_PATH = pathlib.Path(__file__).resolve().parent / "lib" / "libattn.so"
+
+ATTN_OK = 0
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+# Every function include/attn.h declares.
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string",
+                    "attn_last_error")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        name = _status_name(status)
+        super().__init__(f"{where} failed: {name}" + (f" ({detail})" if detail else ""))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise RuntimeError(f"HIP attention library not found at {LIB_PATH}; "
+                           "build it with exact_attention_24_amd.build.build()")
+    L = ctypes.CDLL(str(LIB_PATH))
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
+    L.attn_fwd.restype = i32
+    L.attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                           i32, i32, i32, i32, i32, f32, i32, vp, vp]
+    L.attn_bwd.restype = i32
+    L.attn_status_string.argtypes = [i32]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_last_error.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _status_name(status: int) -> str:
+    try:
+        return lib().attn_status_string(status).decode()
+    except Exception:  # noqa: BLE001 - naming only
+        return f"status {status}"
+
+
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != ATTN_OK:
+        detail = lib().attn_last_error().decode()
+        raise AttnError(status, where, detail)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _stream_handle(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_tensor(name: str, t, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _seqlens_ptr(seqlens, B, device) -> int:
+    import torch
+    if seqlens is None:
+        return 0
+    _check_tensor("seqlens", seqlens, (B,), torch.int32, device)
+    return seqlens.data_ptr()
+
+
+def attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
+             seqlens=None, out=None, lse=None, return_lse: bool = True):
+    """O = softmax(scale * Q K^T) V over [B, H, N, d] device tensors.
+
+    Returns (O, LSE) with LSE fp32 [B, H, N] (natural log), or O alone when
+    ``return_lse`` is False and no ``lse`` buffer is given.
+    """
+    import torch
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, (B, H, N, d), q.dtype, dev)
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, (B, H, N, d), q.dtype, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check_tensor("lse", lse, (B, H, N), torch.float32, dev)
+    st = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                        lse.data_ptr() if lse is not None else 0, B, H, N, d, code,
+                        float(scale), int(bool(causal)), _seqlens_ptr(seqlens, B, dev),
+                        _stream_handle(dev))
+    _check(st, "attn_fwd")
+    return (out, lse) if lse is not None else out
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int, dtype_code: int = DTYPE_BF16) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, H, N, d, dtype_code))
+
+
+def attn_bwd(q, k, v, o, do, lse, *, scale: Optional[float] = None, causal: bool = False,
+             seqlens=None, dq=None, dk=None, dv=None, workspace=None):
+    """Recompute-based backward. Returns (dQ, dK, dV) in the input dtype."""
+    import torch
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_tensor(name, t, (B, H, N, d), q.dtype, dev)
+    _check_tensor("lse", lse, (B, H, N), torch.float32, dev)
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, (B, H, N, d), q.dtype, dev)
+    need = attn_bwd_workspace_bytes(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device buffer")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                        workspace.data_ptr(), nbytes, B, H, N, d, code, float(scale),
+                        int(bool(causal)), _seqlens_ptr(seqlens, B, dev), _stream_handle(dev))
+    _check(st, "attn_bwd")
+    return dq, dk, dv

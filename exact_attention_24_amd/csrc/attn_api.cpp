@@ -1,0 +1,119 @@
+// C-ABI entry points (declared in include/attn.h): argument validation on the
+// host, then dispatch to the gfx950 kernels on the caller's stream. Nothing
+// here allocates device memory or synchronises.
+#include "../../include/attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "attn_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void record_hip_error(hipError_t e, const char* where) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+attn_status check_sizes(int B, int H, int N, int d, attn_dtype dtype) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // Workgroup counts and per-head row offsets must fit the kernels' 32-bit
+  // index arithmetic: (B*H) * ceil(N/64) workgroups and N*d elements per head.
+  const long long heads = (long long)B * H;
+  const long long tiles = heads * ((N + 63) / 64);
+  if (tiles > 0x7fffffffLL || (long long)N * d > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+  }
+  return "ATTN_STATUS_UNKNOWN";
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                     int N, int d, attn_dtype dtype, float scale, int causal,
+                     const int32_t* seqlens, attn_stream_t stream) {
+  attn_status st = check_sizes(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return ATTN_ERR_INVALID_ARG;
+  if ((lse && !aligned(lse, 4)) || (seqlens && !aligned(seqlens, 4))) return ATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+
+  attn::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.seqlens = seqlens;
+  a.B = B; a.H = H; a.N = N;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == ATTN_DTYPE_BF16 ? attn::launch_fwd_bf16(a, d, causal != 0, s)
+                                          : attn::launch_fwd_f32(a, d, causal != 0, s);
+  if (e != hipSuccess) {
+    record_hip_error(e, "attn_fwd launch");
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype dtype) {
+  if (check_sizes(B, H, N, d, dtype) != ATTN_OK) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return ((rows * sizeof(float) + 255) / 256) * 256;
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, int B, int H, int N, int d, attn_dtype dtype,
+                     float scale, int causal, const int32_t* seqlens, attn_stream_t stream) {
+  attn_status st = check_sizes(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !workspace)
+    return ATTN_ERR_INVALID_ARG;
+  const void* t16[] = {q, k, v, o, dO, dq, dk, dv};
+  for (const void* p : t16)
+    if (!aligned(p, 16)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(lse, 4) || !aligned(workspace, 256) || (seqlens && !aligned(seqlens, 4)))
+    return ATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d, dtype)) return ATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+
+  attn::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.delta = (float*)workspace;
+  a.seqlens = seqlens;
+  a.B = B; a.H = H; a.N = N;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = attn::launch_bwd_bf16(a, d, causal != 0, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    record_hip_error(e, "attn_bwd launch");
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+}  // extern "C"

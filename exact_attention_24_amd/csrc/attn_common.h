@@ -1,0 +1,100 @@
+// Device helpers shared by the gfx950 attention kernels: vector types, MFMA
+// wrappers, LDS access through address-space-3 pointers, lane exchanges and
+// bf16 packing. Everything here is written for CDNA4 (wave64, gfx950) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+typedef __bf16 bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+typedef ATTN_LDS char lds_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite initial row maximum: below any real score, so exp2 of the rescale
+// factor underflows to 0 instead of forming (-inf) - (-inf).
+constexpr float kMaxInit = -1.0e30f;
+
+// D += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.
+// A: lane l holds row l%32, k = 8*(l/32) .. +7.  B: lane l holds column l%32,
+// k = 8*(l/32) .. +7.  D: lane l holds column l%32, rows (i/4)*8 + 4*(l/32) + i%4.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---- LDS access (address space 3, so the compiler emits ds_* instructions)
+__device__ __forceinline__ lds_t* lds_base(char* generic) { return (lds_t*)generic; }
+
+__device__ __forceinline__ u32x4 lds_load16(const lds_t* p) { return *(const ATTN_LDS u32x4*)p; }
+__device__ __forceinline__ void lds_store16(lds_t* p, u32x4 v) { *(ATTN_LDS u32x4*)p = v; }
+__device__ __forceinline__ u32x2 lds_load8(const lds_t* p) { return *(const ATTN_LDS u32x2*)p; }
+__device__ __forceinline__ void lds_store8(lds_t* p, u32x2 v) { *(ATTN_LDS u32x2*)p = v; }
+__device__ __forceinline__ float lds_loadf(const lds_t* p) { return *(const ATTN_LDS float*)p; }
+__device__ __forceinline__ void lds_storef(lds_t* p, float v) { *(ATTN_LDS float*)p = v; }
+
+// Transposing LDS read of four 16-bit values. Within each group of 16 lanes,
+// let M[src][s] be the four values at lane src's address; lane j receives
+// M[(j >> 2) + 4*s][j & 3] for s = 0..3.
+__device__ __forceinline__ u32x2 lds_load_tr16(const lds_t* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ bf16x8 join_bf16x8(u32x2 lo, u32x2 hi) {
+  u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return as_bf16x8(v);
+}
+
+// ---- global access
+__device__ __forceinline__ u32x4 gload16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void gstore16(void* p, u32x4 v) { *(u32x4*)p = v; }
+__device__ __forceinline__ void gstore8(void* p, u32x2 v) { *(u32x2*)p = v; }
+
+// ---- lane exchange between the two 32-lane halves of a wave
+// v_permlane32_swap on two copies of x leaves the low half's values in the
+// first result and the high half's in the second, in every lane: lane l sees
+// x[l % 32] and x[l % 32 + 32].
+__device__ __forceinline__ void split_halves(float x, float& lo, float& hi) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  lo = __builtin_bit_cast(float, (uint32_t)r[0]);
+  hi = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Combine the values of lanes l and l ^ 32; both lanes get the same bits.
+__device__ __forceinline__ float max_halves(float x) {
+  float lo, hi;
+  split_halves(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float lo, hi;
+  split_halves(x, lo, hi);
+  return lo + hi;
+}
+
+// ---- bf16 packing (v_cvt_pk_bf16_f32: round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16_t a = (bf16_t)lo, b = (bf16_t)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace attn

@@ -1,0 +1,50 @@
+// Internal interface between the C-ABI layer (attn_api.cpp) and the kernel
+// translation units. Not installed; the public interface is include/attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;               // may be null
+  const int32_t* seqlens;   // may be null
+  int B, H, N;
+  float scale;              // softmax scale applied to q.k
+  float scale_log2;         // scale * log2(e)
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;             // workspace: rowsum(dO o O), fp32 [B,H,N]
+  const int32_t* seqlens;
+  int B, H, N;
+  float scale;
+  float scale_log2;
+};
+
+// Each launcher enqueues its kernels on `stream` and returns the launch status.
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+
+// Host-side mirror of the workgroup -> (head, row tile) order used by the
+// forward kernels (exposed for tests of the scheduling logic).
+void tile_order_host(int block, int num_tiles, int num_heads, bool heavy_first, int* head,
+                     int* tile);
+
+}  // namespace attn

@@ -1,0 +1,133 @@
+/*
+ * attn.h - C ABI of an exact-attention library for AMD MI355X (gfx950).
+ *
+ * The library computes exact scaled dot-product attention
+ *
+ *     O = softmax(scale * Q K^T) V
+ *
+ * the FlashAttention way: Q is cut into row tiles, each tile streams over K/V
+ * tiles held on chip, and an online-softmax state (running row max m, running
+ * exponential sum l, unnormalised output accumulator) is rescaled by
+ * exp(m_old - m_new) whenever the max grows, so the N x N score and probability
+ * matrices never reach device memory. The result equals standard attention up
+ * to floating-point rounding order.
+ *
+ * Pages this interface follows (cited by title):
+ *  - "FlashAttention：从 Safe Softmax 到分块计算": §1 (the definition),
+ *    §3.1-§3.2 (the (m, l, u) state and its merge rule), §5 (tiling), §5.2
+ *    (causal mask: query i sees keys j <= i), §7 (forward loop, rows with no
+ *    visible key in a tile are left untouched), §8 (a per-row log-sum-exp saved
+ *    for a recompute-based backward).
+ *  - "Attention 算子优化:从物化 N×N 矩阵到 FlashAttention 与 PagedAttention":
+ *    §二 (a padded variable-length batch with a key-padding mask), §四 (causal
+ *    block skipping; the backward recomputes P from Q, K, V).
+ *  - the AIInfra FlashAttention note on dpshk.com: §2.1 (finite initial row
+ *    max), §2.3 (dV = P^T dO, dS = P o (dP - rowsum(dP o P)), dP = dO V^T).
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are [B, H, N, d], contiguous, d fastest (element (b,h,i,c) sits at
+ *    ((b*H + h)*N + i)*d + c). Q, K, V, O, dO, dQ, dK, dV share one shape.
+ *  - All tensor pointers are DEVICE pointers. The caller allocates and owns
+ *    every buffer; the library allocates nothing and keeps no state between
+ *    calls. Buffers must be 16-byte aligned.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream). No entry point synchronises the host.
+ *  - Argument errors are detected on the host before anything is launched and
+ *    are returned as a status; nothing is thrown across the ABI. A failed HIP
+ *    launch returns ATTN_ERR_HIP.
+ *  - seqlens: optional DEVICE int32 array [B]. Sequence b has L_b valid
+ *    positions (queries and keys alike); positions >= L_b are padding. Query
+ *    rows >= L_b are not computed: their O (and dQ) rows are written as 0 and
+ *    their LSE as -inf; keys >= L_b get zero weight (and zero dK, dV). NULL
+ *    means L_b = N for every b. Values must lie in [0, N]; values outside are
+ *    clamped into [0, N] by the kernels (the host cannot check device memory
+ *    without a synchronisation).
+ *  - causal != 0 masks keys j > i for query i (top-left alignment, within
+ *    each sequence's valid length). Both masks may be combined.
+ *  - scale must be finite and > 0 (usually 1/sqrt(d)).
+ */
+#ifndef EXACT_ATTENTION_ATTN_H
+#define EXACT_ATTENTION_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t* attn_stream_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad scale, misalignment */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid request this library does not implement (e.g. d not in {64,128}) */
+  ATTN_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
+} attn_status;
+
+typedef enum {
+  ATTN_DTYPE_F32 = 0,  /* fp32 storage, fp32 arithmetic throughout */
+  ATTN_DTYPE_BF16 = 1  /* bf16 storage; products on bf16 MFMA with fp32 accumulation;
+                          softmax in fp32; outputs rounded to bf16 (nearest-even) */
+} attn_dtype;
+
+/*
+ * attn_fwd - attention forward.
+ *
+ * Computes, per (b, h) and valid query row i, O_i = sum_j P_ij V_j with
+ * P_ij = exp(scale*q_i.k_j - LSE_i) over the visible keys j, and
+ * LSE_i = ln(sum_j exp(scale*q_i.k_j)) (natural log).
+ *
+ *  q, k, v   [B,H,N,d] of `dtype`, read only.
+ *  o         [B,H,N,d] of `dtype`, written (padded rows written as 0).
+ *  lse       [B,H,N] fp32, written; may be NULL when no backward will follow.
+ *  B, H, N   >= 1.   d: 64 or 128 (ATTN_ERR_UNSUPPORTED otherwise).
+ *
+ * The bf16 forward is deterministic: the same inputs give bit-identical outputs.
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N, int d, attn_dtype dtype, float scale, int causal,
+                     const int32_t* seqlens, attn_stream_t stream);
+
+/*
+ * attn_bwd_workspace_bytes - device workspace that attn_bwd needs for these sizes
+ * (it holds D_i = rowsum(dO_i o O_i), fp32 [B,H,N]). Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype dtype);
+
+/*
+ * attn_bwd - recompute-based attention backward.
+ *
+ * Given the forward's inputs q, k, v, its output o and lse, and the upstream
+ * gradient dO, recomputes P tile by tile from q, k and lse and writes
+ *   dV = P^T dO,   dP = dO V^T,   D_i = rowsum(dO_i o O_i) (= rowsum(dP o P)),
+ *   dS = P o (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
+ *
+ *  q, k, v, o, dO   [B,H,N,d] of `dtype`, read only.
+ *  lse              [B,H,N] fp32 from attn_fwd with the same arguments.
+ *  dq, dk, dv       [B,H,N,d] of `dtype`, written (fully overwritten).
+ *  workspace        device buffer of at least attn_bwd_workspace_bytes(...)
+ *                   bytes, 256-byte aligned; contents on entry are ignored.
+ *  workspace_bytes  its size; smaller than required gives ATTN_ERR_INVALID_ARG.
+ * Only ATTN_DTYPE_BF16 is implemented (ATTN_ERR_UNSUPPORTED for fp32).
+ * Deterministic: no atomics are used.
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, int B, int H, int N, int d, attn_dtype dtype,
+                     float scale, int causal, const int32_t* seqlens, attn_stream_t stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* attn_status_string(attn_status s);
+
+/* Message of the last HIP error seen by this library on the calling thread
+ * ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_ATTN_H */

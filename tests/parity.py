@@ -1,0 +1,55 @@
+"""Shared tolerances and comparison metrics for the GPU parity tests.
+
+Metrics follow the AIInfra FlashAttention note (dpshk.com, §3.1): max absolute
+error, max relative error, cosine similarity and the NaN/Inf count are all
+recorded; the pass/fail bar is max absolute error for outputs and relative
+Frobenius error for gradients:
+  O:   fp32 inputs <= 1e-5, bf16 inputs <= 2e-2 (oracle fed the same bf16 values)
+  LSE: fp32 <= 1e-5, bf16 <= 1e-3 (LSE sits before the bf16 output rounding, so
+       its error is that of fp32 score accumulation)
+  dQ, dK, dV: ||g - g_ref||_F / ||g_ref||_F <= 5e-2 per tensor.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+O_TOL = {"f32": 1e-5, "bf16": 2e-2}
+LSE_TOL = {"f32": 1e-5, "bf16": 1e-3}
+GRAD_REL_FRO = 5e-2
+
+
+def dtype_name(t: torch.Tensor) -> str:
+    return "f32" if t.dtype == torch.float32 else "bf16"
+
+
+def to_np(t) -> np.ndarray:
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64)
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def metrics(got, ref) -> dict:
+    g, r = to_np(got), to_np(ref)
+    fin = np.isfinite(r)
+    bad = int(np.sum(~np.isfinite(g[fin])))
+    diff = np.abs(g[fin] - r[fin]) if fin.any() else np.zeros(1)
+    denom = np.maximum(np.abs(r[fin]), 1e-6) if fin.any() else np.ones(1)
+    gv, rv = g[fin].ravel(), r[fin].ravel()
+    nrm = np.linalg.norm(gv) * np.linalg.norm(rv)
+    return {"max_abs": float(diff.max()), "max_rel": float((diff / denom).max()),
+            "cos": float(gv @ rv / nrm) if nrm > 0 else 1.0, "nonfinite": bad,
+            "inf_mismatch": int(np.sum(np.isfinite(g) != fin))}
+
+
+def assert_close(got, ref, tol: float, what: str) -> dict:
+    m = metrics(got, ref)
+    assert m["nonfinite"] == 0, f"{what}: {m['nonfinite']} NaN/Inf where the oracle is finite ({m})"
+    assert m["inf_mismatch"] == 0, f"{what}: finiteness pattern differs from the oracle ({m})"
+    assert m["max_abs"] <= tol, f"{what}: max abs err {m['max_abs']:.3e} > {tol:.1e} ({m})"
+    return m
+
+
+def rel_fro(got, ref) -> float:
+    g, r = to_np(got), to_np(ref)
+    return float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))

@@ -1,0 +1,120 @@
+"""CPU checks of the C-ABI library: it loads, exports every function that
+include/attn.h declares, and its host-side argument validation returns the
+documented status codes. Nothing here launches a kernel: every call below is
+rejected on the host before any HIP call is made."""
+import ctypes
+import pathlib
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_24_amd as ea
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "attn.h"
+
+OK, INVALID, UNSUPPORTED, HIP = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not ea.LIB_PATH.exists():
+        pytest.fail(f"{ea.LIB_PATH} is missing: run __graft_entry__.build() first")
+    return ea.lib()
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(ea.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", str(ea.LIB_PATH)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, f"{name} is not a defined dynamic symbol (C linkage)"
+
+
+def test_status_strings(L):
+    assert ea.attn_status_string(OK) == "ATTN_OK"
+    assert ea.attn_status_string(INVALID) == "ATTN_ERR_INVALID_ARG"
+    assert ea.attn_status_string(UNSUPPORTED) == "ATTN_ERR_UNSUPPORTED"
+    assert ea.attn_status_string(HIP) == "ATTN_ERR_HIP"
+    assert ea.attn_status_string(77) == "ATTN_STATUS_UNKNOWN"
+    assert L.attn_last_error() == b""
+
+
+# Fake, 16-byte-aligned "device" addresses: never dereferenced, because every
+# call below fails validation first.
+P = 0x10000
+
+
+def fwd(L, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=64, d=64, dtype=1, scale=0.125, causal=0,
+        seqlens=0):
+    return L.attn_fwd(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, seqlens, 0)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=0), INVALID), (dict(k=0), INVALID), (dict(v=0), INVALID), (dict(o=0), INVALID),
+    (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(N=0), INVALID), (dict(d=0), INVALID),
+    (dict(dtype=7), INVALID), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(d=32), UNSUPPORTED), (dict(scale=0.0), INVALID), (dict(scale=-1.0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(q=P + 8), INVALID), (dict(o=P + 4), INVALID), (dict(lse=P + 2), INVALID),
+    (dict(seqlens=P + 1), INVALID), (dict(B=1 << 20, H=1 << 12, N=1 << 12), UNSUPPORTED),
+])
+def test_fwd_rejects_bad_arguments(L, kw, want):
+    # scale and null-pointer checks come after size checks; each case fails exactly one rule
+    assert fwd(L, **kw) == want
+
+
+def bwd(L, ws_bytes=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P, B=1, H=1, N=64, d=64,
+             dtype=1, scale=0.125, causal=0, seqlens=0)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = L.attn_bwd_workspace_bytes(a["B"], a["H"], a["N"], a["d"], a["dtype"])
+    return L.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                      a["dv"], a["ws"], ws_bytes, a["B"], a["H"], a["N"], a["d"], a["dtype"],
+                      a["scale"], a["causal"], a["seqlens"], 0)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(do=0), INVALID), (dict(lse=0), INVALID), (dict(dq=0), INVALID), (dict(ws=0), INVALID),
+    (dict(dk=P + 8), INVALID), (dict(ws=P + 16), INVALID), (dict(d=80), UNSUPPORTED),
+    (dict(ws_bytes=16), INVALID), (dict(scale=0.0), INVALID), (dict(dtype=0), UNSUPPORTED),
+    (dict(N=-5), INVALID),
+])
+def test_bwd_rejects_bad_arguments(L, kw, want):
+    ws_bytes = kw.pop("ws_bytes", None)
+    assert bwd(L, ws_bytes, **kw) == want
+
+
+def test_workspace_bytes(L):
+    assert L.attn_bwd_workspace_bytes(2, 16, 8192, 128, 1) == 2 * 16 * 8192 * 4
+    assert L.attn_bwd_workspace_bytes(1, 1, 3, 64, 1) == 256  # rounded up to 256 bytes
+    assert L.attn_bwd_workspace_bytes(1, 1, 0, 64, 1) == 0
+    assert L.attn_bwd_workspace_bytes(1, 1, 8, 100, 1) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ea.attn_fwd(x, x, x)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(ea, "_lib", None)
+    monkeypatch.setattr(ea, "LIB_PATH", tmp_path / "nope.so")
+    with pytest.raises(RuntimeError, match="not found"):
+        ea.lib()
