@@ -58,6 +58,20 @@ def cpu_baseline(x, w, budget_s: float):
                       f"{os.cpu_count()}"}
 
 
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration(torch, steps):
+    """Copy a 256 MiB buffer `steps` times (reads and writes 256 MiB per launch)."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read_per_launch": COPY_BYTES,
+                      "bytes_written_per_launch": COPY_BYTES, "launches": steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -65,6 +79,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 disables it)")
+    ap.add_argument("--mode", choices=["fwd", "copy"], default="fwd",
+                    help="fwd: the benchmark; copy: a plain device copy of known size, whose "
+                         "FETCH_SIZE/WRITE_SIZE counters calibrate the traffic figure")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -72,6 +89,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.mode == "copy":
+        copy_calibration(torch, args.steps)
+        return
     import exact_attention_24_amd as ea
     from attn_inputs import WORKLOADS, make_workload_inputs
 

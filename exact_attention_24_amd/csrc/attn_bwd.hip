@@ -23,50 +23,13 @@
 #include "attn_common.h"
 #include "attn_kernels.h"
 #include "attn_sched.h"
+#include "attn_tile.h"
 
 #include <math.h>
 
 namespace attn {
 
 namespace {
-
-// Row-major [rows][D] bf16 tile in LDS with no padding; the 16-byte chunk c of
-// row r is stored at chunk c ^ swz(r). The XOR keeps both access patterns
-// bank-conflict free on gfx950's 64 banks: 16 consecutive rows read at one
-// chunk (ds_read_b128 MFMA operands), and 4 consecutive rows read as 4
-// consecutive chunks (the ds_read_b64_tr_b16 transposed operands).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-template <int D>
-__device__ __forceinline__ int tile_off(int r, int chunk) {
-  return r * (D * 2) + ((chunk ^ swz<D>(r)) << 4);
-}
-// Byte offset of element column `col` (a multiple of 4) of row r.
-template <int D>
-__device__ __forceinline__ int tile_off_col(int r, int col) {
-  return tile_off<D>(r, col >> 3) + ((col >> 2) & 1) * 8;
-}
-
-// Transposed MFMA operand from a row-major tile: lane gets the 8 values
-// T[row0 + hi*4 + {0..3}, 8 + hi*4 + {0..3}][col0 + lane%32] in the key order of
-// a 32x32 accumulator's lanes (see the forward kernel).
-template <int D>
-__device__ __forceinline__ bf16x8 tr_operand(const lds_t* tile, int row0, int col0, int lane) {
-  const int r = row0 + (lane >> 5) * 4 + ((lane & 15) >> 2);
-  const int col = col0 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-  const u32x2 lo = lds_load_tr16(tile + tile_off_col<D>(r, col));
-  const u32x2 up = lds_load_tr16(tile + tile_off_col<D>(r + 8, col));
-  return join_bf16x8(lo, up);
-}
-
-__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int h) {
-  u32x4 w = {pack_bf16x2(s[8 * h + 0], s[8 * h + 1]), pack_bf16x2(s[8 * h + 2], s[8 * h + 3]),
-             pack_bf16x2(s[8 * h + 4], s[8 * h + 5]), pack_bf16x2(s[8 * h + 6], s[8 * h + 7])};
-  return as_bf16x8(w);
-}
 
 __device__ __forceinline__ int seq_len(const BwdArgs& a, int b) {
   return a.seqlens ? min(max(a.seqlens[b], 0), a.N) : a.N;

@@ -18,6 +18,7 @@
 #include "attn_common.h"
 #include "attn_kernels.h"
 #include "attn_sched.h"
+#include "attn_tile.h"
 
 #include <math.h>
 
@@ -29,30 +30,41 @@ namespace {
 // bf16 inputs, MFMA products, fp32 softmax and accumulation.
 //
 // Workgroup: 4 waves, 128 query rows (32 per wave), K/V tiles of 64 keys,
-// double-buffered in LDS. Scores are computed transposed, S^T = K Q^T, with
-// v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand and Q (held in
-// VGPRs for the whole loop) is the B operand, so each lane's accumulator holds
-// 16 keys of ONE query. Row max and row sum are then 32 in-lane operations plus
-// one exchange between the two 32-lane halves. The output is accumulated
-// transposed as well, O^T += V^T P^T: P^T stays in the accumulator lanes it
-// was computed in (B operand), and V^T is read from the row-major V tile with
-// the transposing LDS load ds_read_b64_tr_b16, in the same key order as P^T's
-// lanes hold. All exponentials are exp2 with log2(e) folded into the scale.
+// double-buffered in LDS and filled by direct global->LDS loads
+// (global_load_lds_dwordx4, no VGPR staging). Scores are computed transposed,
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand and
+// Q (held in VGPRs for the whole loop) is the B operand, so each lane's
+// accumulator holds keys of ONE query. Row max and row sum are in-lane
+// operations plus one exchange between the two 32-lane halves. The output is
+// accumulated transposed as well, O^T += V^T P^T: P^T stays in the lanes it was
+// computed in (B operand) and V^T is read from the row-major V tile with the
+// transposing LDS load, in the key order P^T's lanes hold.
+//
+// Softmax arithmetic per score: one FMA (s*scale*log2e - m*scale*log2e), one
+// v_exp_f32 (exp2), one fp32 add into the row sum, and a share of a v_max3 and
+// of a bf16 pack; statistics stay in fp32 and only the P V product sees bf16
+// weights. The rescale of [SafeSoftmax] §3.2 is
+// applied lazily: the reference max m only moves when the tile max exceeds it
+// by more than 2^8 in exp2 units (weights stay <= 256, far from fp32 or bf16
+// range limits), so once a row's max has settled the O accumulator is not
+// touched. O / l and LSE use the same reference, so the result is the same
+// softmax.
 // ----------------------------------------------------------------------------
+constexpr float kLazyRescale = 8.0f;  // log2 of the largest unnormalised weight
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   constexpr int BM = 128, BN = 64;
-  constexpr int KS = D * 2 + 16;      // K row stride in LDS (bytes): 16 consecutive rows hit distinct banks
-  constexpr int VS = D * 2 + 64;      // V row stride in LDS (bytes), for the transposing reads
-  constexpr int KB = BN * KS, VB = BN * VS, STAGE = KB + VB;
+  constexpr int TILE = BN * D * 2;
+  constexpr int STAGE = 2 * TILE;     // K tile, then V tile
   constexpr int CH = D / 8;           // 16-byte chunks per row
-  constexpr int LOADS = BN * CH / 256;
   constexpr int DS = D / 16, DB = D / 32;
 
   extern __shared__ __attribute__((aligned(16))) char smem_generic[];
   lds_t* smem = lds_base(smem_generic);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int N = a.N;
   const int nm = (N + BM - 1) / BM;
@@ -64,8 +76,6 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   const int m0 = mt * BM;
   const size_t hoff = (size_t)bh * N * D;
   const bf16_t* __restrict__ Qh = (const bf16_t*)a.q + hoff;
-  const bf16_t* __restrict__ Kh = (const bf16_t*)a.k + hoff;
-  const bf16_t* __restrict__ Vh = (const bf16_t*)a.v + hoff;
   bf16_t* __restrict__ Oh = (bf16_t*)a.o + hoff;
   float* __restrict__ lse_h = a.lse ? a.lse + (size_t)bh * N : nullptr;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -86,125 +96,103 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   const int w_end = (qw >= L) ? 0 : (CAUSAL ? min(L, qw + 32) : L);
   const int wnt = (w_end + BN - 1) / BN;                 // tiles this wave computes
 
+  const TileDma<D, BN, 4> kdma((const bf16_t*)a.k + hoff, N, wave, lane);
+  const TileDma<D, BN, 4> vdma((const bf16_t*)a.v + hoff, N, wave, lane);
+  kdma.load(smem, 0);
+  vdma.load(smem + TILE, 0);
+
   // Q rows -> VGPRs, B-operand layout: lane holds query q, d = 16*ds + 8*hi .. +7.
   bf16x8 qr[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds)
     qr[ds] = as_bf16x8(q < N ? gload16(Qh + (size_t)q * D + ds * 16 + hi * 8) : zero4);
 
-  u32x4 kr[LOADS], vr[LOADS];
-  auto gload_tile = [&](int n0) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i, row = c / CH, col = c % CH, g = n0 + row;
-      kr[i] = g < N ? gload16(Kh + (size_t)g * D + col * 8) : zero4;
-      vr[i] = g < N ? gload16(Vh + (size_t)g * D + col * 8) : zero4;
-    }
-  };
-  auto lds_store_tile = [&](int st) {
-    lds_t* kb = smem + st * STAGE;
-    lds_t* vb = kb + KB;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i, row = c / CH, col = c % CH;
-      lds_store16(kb + row * KS + col * 16, kr[i]);
-      lds_store16(vb + row * VS + col * 16, vr[i]);
-    }
-  };
-
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m_run = kMaxInit, l_run = 0.f;
+  float m_ref = kMaxInit, l_part = 0.f;
   const float c2 = a.scale_log2;
 
-  // Lane-constant parts of the LDS addresses.
-  const int k_lane = l32 * KS + hi * 16;
-  const int v_lane = (hi * 4 + ((lane & 15) >> 2)) * VS + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
-
-  gload_tile(0);
-  lds_store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < nt; ++j) {
-    const int st = j & 1, n0 = j * BN;
-    if (j + 1 < nt) gload_tile(n0 + BN);
+  // One KV tile: j is the tile index, ST the LDS stage it is in. The two calls
+  // below pass literal stages and are inlined, so every LDS address is a
+  // loop-invariant register plus an immediate offset.
+  auto tile_step = [&](int j, const int ST) {
+    const int n0 = j * BN;
+    if (j + 1 < nt) {
+      kdma.load(smem + (ST ^ 1) * STAGE, n0 + BN);
+      vdma.load(smem + (ST ^ 1) * STAGE + TILE, n0 + BN);
+    }
     if (j < wnt) {
-      const lds_t* kb = smem + st * STAGE;
-      const lds_t* vb = kb + KB;
+      const lds_t* kt = smem + ST * STAGE;
+      const lds_t* vt = kt + TILE;
       // S^T (64 keys x 32 queries) as two 32x32 blocks.
-      f32x16 s0, s1;
+      f32x16 s0 = mfma32x32x16_z(row_operand<D>(kt, 0, 0, lane), qr[0]);
+      f32x16 s1 = mfma32x32x16_z(row_operand<D>(kt, 32, 0, lane), qr[0]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const bf16x8 k0 = as_bf16x8(lds_load16(kb + k_lane + ds * 32));
-        const bf16x8 k1 = as_bf16x8(lds_load16(kb + k_lane + 32 * KS + ds * 32));
-        s0 = mfma32x32x16(k0, qr[ds], s0);
-        s1 = mfma32x32x16(k1, qr[ds], s1);
+      for (int ds = 1; ds < DS; ++ds) {
+        s0 = mfma32x32x16(row_operand<D>(kt, 0, ds * 2, lane), qr[ds], s0);
+        s1 = mfma32x32x16(row_operand<D>(kt, 32, ds * 2, lane), qr[ds], s1);
       }
-      // Mask keys past the valid length and, for causal, keys after the query.
+      // Key n0 + hi*4 + c (c = (i/4)*8 + i%4, +32 for s1) is visible iff c <= lim.
       if (n0 + BN > L || (CAUSAL && n0 + BN - 1 > qw)) {
+        const int lim = (CAUSAL ? min(q, L - 1) : L - 1) - n0 - hi * 4;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = n0 + (i >> 2) * 8 + hi * 4 + (i & 3);
-          if (key >= L || (CAUSAL && key > q)) s0[i] = -INFINITY;
-          if (key + 32 >= L || (CAUSAL && key + 32 > q)) s1[i] = -INFINITY;
+          const int c = (i >> 2) * 8 + (i & 3);
+          s0[i] = c <= lim ? s0[i] : -INFINITY;
+          s1[i] = c + 32 <= lim ? s1[i] : -INFINITY;
         }
       }
-      float mx = fmaxf(s0[0], s1[0]);
+      float mx = max3f(s0[0], s0[1], s1[0]);
+      mx = max3f(mx, s1[1], s0[2]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+      for (int i = 2; i < 15; ++i) mx = max3f(mx, s1[i], s0[i + 1]);
+      mx = fmaxf(mx, s1[15]);
       mx = max_halves(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float mc = m_new * c2;
-      const float alpha = fast_exp2((m_run - m_new) * c2);
-      float ls = 0.f;
+      if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c2 > kLazyRescale)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = fast_exp2((m_ref - m_new) * c2);
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        m_ref = m_new;
+      }
+      const float mc = m_ref * c2;
+      float sa = 0.f, sb = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         s0[i] = fast_exp2(fmaf(s0[i], c2, -mc));
         s1[i] = fast_exp2(fmaf(s1[i], c2, -mc));
-        ls += s0[i] + s1[i];
+        sa += s0[i];
+        sb += s1[i];
       }
-      l_run = alpha * l_run + ls;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      l_part += sa + sb;
       // P^T -> bf16 B operands, one per 16-key step.
-      bf16x8 pb[4];
+      const bf16x8 pb[4] = {pack8(s0, 0), pack8(s0, 1), pack8(s1, 0), pack8(s1, 1)};
+      // O^T (D x 32) += V^T (D x 64) P^T (64 x 32).
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4 w0 = {pack_bf16x2(s0[8 * h + 0], s0[8 * h + 1]), pack_bf16x2(s0[8 * h + 2], s0[8 * h + 3]),
-                    pack_bf16x2(s0[8 * h + 4], s0[8 * h + 5]), pack_bf16x2(s0[8 * h + 6], s0[8 * h + 7])};
-        u32x4 w1 = {pack_bf16x2(s1[8 * h + 0], s1[8 * h + 1]), pack_bf16x2(s1[8 * h + 2], s1[8 * h + 3]),
-                    pack_bf16x2(s1[8 * h + 4], s1[8 * h + 5]), pack_bf16x2(s1[8 * h + 6], s1[8 * h + 7])};
-        pb[h] = as_bf16x8(w0);
-        pb[2 + h] = as_bf16x8(w1);
-      }
-      // O^T (D x 32) += V^T (D x 64) P^T (64 x 32). For key step ks the lane
-      // half hi holds keys ks*16 + hi*4 + {0..3} and ks*16 + 8 + hi*4 + {0..3};
-      // the two transposing reads fetch exactly those keys of V for d = lane%32.
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const lds_t* p = vb + v_lane + ks * 16 * VS + db * 64;
-          const u32x2 lo = lds_load_tr16(p);
-          const u32x2 up = lds_load_tr16(p + 8 * VS);
-          o[db] = mfma32x32x16(join_bf16x8(lo, up), pb[ks], o[db]);
-        }
-      }
+        for (int db = 0; db < DB; ++db)
+          o[db] = mfma32x32x16(tr_operand<D>(vt, ks * 16, db * 32, lane), pb[ks], o[db]);
     }
-    if (j + 1 < nt) lds_store_tile(st ^ 1);
+    dma_wait();
     __syncthreads();
+  };
+
+  dma_wait();
+  __syncthreads();
+  for (int j = 0; j < nt; j += 2) {
+    tile_step(j, 0);
+    if (j + 1 < nt) tile_step(j + 1, 1);
   }
 
   // Epilogue: O = O_acc / l, rounded to bf16; LSE = m*scale + ln l.
-  const float l_tot = sum_halves(l_run);
+  const float l_tot = sum_halves(l_part);
   const bool valid = q < L && l_tot > 0.f;
   const float inv = valid ? 1.f / l_tot : 0.f;
   if (q < N) {
@@ -217,8 +205,17 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
                          pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
         gstore8(orow + db * 32 + g * 8 + hi * 4, w);
       }
-    if (lse_h && hi == 0) lse_h[q] = valid ? m_run * a.scale + logf(l_tot) : -INFINITY;
+    if (lse_h && hi == 0) lse_h[q] = valid ? m_ref * a.scale + logf(l_tot) : -INFINITY;
   }
+}
+
+// The kernel is a thin wrapper: with the body in a __device__ template, the
+// host compilation pass emits every instantiation's launch stub (with the
+// buffer-load builtins directly in a __global__ template body it silently
+// dropped some of them).
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
+  fwd_bf16_body<D, CAUSAL>(a);
 }
 
 // ----------------------------------------------------------------------------
@@ -322,7 +319,7 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a) {
 template <int D, bool CAUSAL>
 hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t stream) {
   constexpr int BM = 128, BN = 64;
-  constexpr int lds = 2 * (BN * (D * 2 + 16) + BN * (D * 2 + 64));
+  constexpr int lds = 2 * 2 * BN * D * 2;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)fwd_bf16_kernel<D, CAUSAL>,

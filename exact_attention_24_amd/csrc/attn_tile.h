@@ -1,0 +1,109 @@
+// LDS tile layout and MFMA operand helpers shared by the forward and backward
+// kernels (gfx950, wave64, v_mfma_f32_32x32x16_bf16).
+#pragma once
+
+#include "attn_common.h"
+
+namespace attn {
+
+// A row-major [rows][D] bf16 tile in LDS, no padding; the 16-byte chunk c of
+// row r sits at chunk c ^ swz(r). The XOR keeps both read patterns free of
+// bank conflicts on gfx950's 64 LDS banks: 16 consecutive rows read at one
+// chunk (ds_read_b128 operands), and 4 consecutive rows read as 4 consecutive
+// chunks (ds_read_b64_tr_b16 transposed operands). It is a bijection on the
+// chunks of each row, so a wave can fill whole rows with one 1 KB
+// global_load_lds_dwordx4 by fetching, for physical chunk p, logical chunk
+// p ^ swz(r).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int chunk) {
+  return r * (D * 2) + ((chunk ^ swz<D>(r)) << 4);
+}
+// Byte offset of element column `col` (a multiple of 4) of row r.
+template <int D>
+__device__ __forceinline__ int tile_off_col(int r, int col) {
+  return tile_off<D>(r, col >> 3) + ((col >> 2) & 1) * 8;
+}
+
+// A operand (32 rows x 16 k) read straight from a tile: lane holds row
+// row0 + lane%32 and k = chunk*8 + 8*(lane/32) .. +7.
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const lds_t* tile, int row0, int chunk, int lane) {
+  return as_bf16x8(lds_load16(tile + tile_off<D>(row0 + (lane & 31), chunk + (lane >> 5))));
+}
+
+// Transposed operand from a row-major tile T (rows = the contraction index):
+// lane receives T[row0 + hi*4 + {0..3}][col] and T[row0 + 8 + hi*4 + {0..3}][col]
+// with col = col0 + lane%32 and hi = lane/32. That is exactly the k order in
+// which a 32x32 accumulator's lane holds its 16 rows (i/4)*8 + hi*4 + i%4, so a
+// score block produced by one MFMA feeds the next MFMA as the other operand
+// without any data exchange between lanes. ds_read_b64_tr_b16 gives lane j of
+// each 16-lane group the values M[(j>>2) + 4s][j&3] (s = 0..3) of the 8-byte
+// pieces M[src] its group addressed, so lane src addresses row
+// row0 + hi*4 + (src>>2) at column col0 + 16*((lane>>4)&1) + 4*(src&3).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const lds_t* tile, int row0, int col0, int lane) {
+  const int r = row0 + (lane >> 5) * 4 + ((lane & 15) >> 2);
+  const int col = col0 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  const u32x2 lo = lds_load_tr16(tile + tile_off_col<D>(r, col));
+  const u32x2 up = lds_load_tr16(tile + tile_off_col<D>(r + 8, col));
+  return join_bf16x8(lo, up);
+}
+
+// Accumulator values 8h .. 8h+7 packed to bf16 (round to nearest even): the
+// B operand for the 16-row k step h of the next product.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int h) {
+  u32x4 w = {pack_bf16x2(s[8 * h + 0], s[8 * h + 1]), pack_bf16x2(s[8 * h + 2], s[8 * h + 3]),
+             pack_bf16x2(s[8 * h + 4], s[8 * h + 5]), pack_bf16x2(s[8 * h + 6], s[8 * h + 7])};
+  return as_bf16x8(w);
+}
+
+// Direct global -> LDS tile loads (buffer_load_dwordx4 ... lds) for one
+// (batch, head). The buffer resource spans exactly the head's N x D elements,
+// so rows past the end read as zeros (hardware range check): the tile never
+// holds stale LDS bytes that could be NaN bit patterns, and no clamping is
+// needed. NWAVES waves share a tile of ROWS rows; the calling wave fills the
+// 1 KB row groups g = wave, wave + NWAVES, ... (64/(D/8) rows each), lane l
+// writing physical chunk l % (D/8) of row l / (D/8), i.e. logical chunk
+// (l % (D/8)) ^ swz(row). The per-lane byte offsets do not depend on which
+// tile is loaded, so they are computed once; the tile's first row enters as a
+// scalar offset.
+template <int D, int ROWS, int NWAVES>
+struct TileDma {
+  static constexpr int CPR = D / 8;      // 16-byte chunks per row
+  static constexpr int RPG = 64 / CPR;   // rows per 1 KB wave load
+  static constexpr int ITER = ROWS / RPG / NWAVES;
+  static_assert(ITER * RPG * NWAVES == ROWS, "tile rows must split evenly over the waves");
+
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[ITER];
+  int wave;
+
+  __device__ __forceinline__ TileDma(const bf16_t* head, int n_rows, int wave_, int lane) {
+    wave = wave_;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)head, (short)0, n_rows * D * 2, 0x00020000);
+    const int rsub = lane / CPR, pc = lane % CPR;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int r = (wave + it * NWAVES) * RPG + rsub;
+      voff[it] = (uint32_t)(r * D * 2 + ((pc ^ swz<D>(r)) << 4));
+    }
+  }
+  // Enqueue the loads of rows [row0, row0 + ROWS) into `tile`.
+  __device__ __forceinline__ void load(lds_t* tile, int row0) const {
+    const uint32_t soff = (uint32_t)row0 * (D * 2);
+#pragma unroll
+    for (int it = 0; it < ITER; ++it)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (ATTN_LDS void*)(tile + (wave + it * NWAVES) * 1024), 16, voff[it], soff, 0, 0);
+  }
+};
+
+// Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0).
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+}  // namespace attn

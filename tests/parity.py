@@ -5,8 +5,9 @@ error, max relative error, cosine similarity and the NaN/Inf count are all
 recorded; the pass/fail bar is max absolute error for outputs and relative
 Frobenius error for gradients:
   O:   fp32 inputs <= 1e-5, bf16 inputs <= 2e-2 (oracle fed the same bf16 values)
-  LSE: fp32 <= 1e-5, bf16 <= 1e-3 (LSE sits before the bf16 output rounding, so
-       its error is that of fp32 score accumulation)
+  LSE: fp32 <= 1e-5, bf16 <= 1e-3 (the softmax statistics are kept in fp32;
+       LSE sits before any bf16 rounding, so its error is that of fp32 score
+       accumulation)
   dQ, dK, dV: ||g - g_ref||_F / ||g_ref||_F <= 5e-2 per tensor. Where the oracle's
        gradient is exactly zero (a single visible key: dS = P o (dP - D) with
        dP = D), the relative error is undefined and the bar is max|g| <= 1e-5,

@@ -92,7 +92,7 @@ def test_two_block_example(dtype):
     o, lse = run_fwd(q, k, v, 1.0)
     l = 2 * math.exp(-2) + math.exp(-1) + 1
     assert abs(math.exp(float(lse[0, 0, 0]) - 3.0) - 1.638) <= 1e-3  # the page's printed value
-    assert abs(float(lse[0, 0, 0]) - (3 + math.log(l))) <= 1e-5
+    assert abs(float(lse[0, 0, 0]) - (3 + math.log(l))) <= LSE_TOL[dtype_name(q)]
     want = (0.5 * math.exp(-2) + 1.0 * math.exp(-1) + 1.5 + 2.0 * math.exp(-2)) / l
     # bf16: O ~ 1.35, half an ulp in [1, 2) is 2^-8, plus 2^-9 * max|V| = 2^-8
     tol = 1e-5 if dtype == torch.float32 else 2 ** -8 + 2 ** -9 * 2
@@ -112,7 +112,7 @@ def test_merge_example(dtype):
     u = math.exp(-1) * (10 * math.exp(-1) + 20) + 30
     tol = 1e-5 if dtype == torch.float32 else 2e-2
     assert abs(float(o[0, 0, 0, 0]) - f * u / l) <= tol
-    assert abs(float(lse[0, 0, 0]) - (3 + math.log(l))) <= 1e-5
+    assert abs(float(lse[0, 0, 0]) - (3 + math.log(l))) <= LSE_TOL[dtype_name(q)]
 
 
 # ----------------------------------------------- small shapes, full comparison
