@@ -59,6 +59,29 @@ def cpu_baseline(x, w, budget_s: float):
 
 
 COPY_BYTES = 256 << 20
+PROFILE = "profiles/fwd_bf16_causal_b2_h32_n4096_d128.md"
+FWD_SOURCES = ["exact_attention_24_amd/csrc/attn_fwd.hip", "exact_attention_24_amd/csrc/attn_common.h",
+               "exact_attention_24_amd/csrc/attn_tile.h", "exact_attention_24_amd/csrc/attn_sched.h"]
+
+
+def profiled_traffic():
+    """HBM-side bytes per launch from the committed counter summary, or None when
+    the forward kernel's sources changed after the counters were taken."""
+    import hashlib
+    import pathlib
+    root = pathlib.Path(__file__).resolve().parent
+    try:
+        text = (root / PROFILE).read_text()
+        h = hashlib.sha256()
+        for s in FWD_SOURCES:
+            h.update((root / s).read_bytes())
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines()
+                  if line.startswith(("traffic_bytes_per_launch: ", "source_sha256_16: ")))
+    if fields.get("source_sha256_16", "").strip() != h.hexdigest()[:16]:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def copy_calibration(torch, steps):
@@ -148,7 +171,7 @@ def main():
                       "p90": round(per[int(0.9 * (len(per) - 1))], 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": profiled_traffic(),
                      "kernel": "fwd_bf16_kernel<128, causal>",
                      "algorithmic": "4*B*H*N^2*d/2 FLOP per launch"},
     }

@@ -56,12 +56,16 @@ template <int D, bool CAUSAL>
 __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   constexpr int BM = 128, BN = 64;
   constexpr int TILE = BN * D * 2;
-  constexpr int STAGE = 2 * TILE;     // K tile, then V tile
   constexpr int CH = D / 8;           // 16-byte chunks per row
   constexpr int DS = D / 16, DB = D / 32;
 
-  extern __shared__ __attribute__((aligned(16))) char smem_generic[];
-  lds_t* smem = lds_base(smem_generic);
+  // One LDS array per (stage, tensor): distinct objects let the compiler see
+  // that reads of one stage never alias the direct-to-LDS loads filling the
+  // other, so it does not stall them on the prefetch (with a single array it
+  // waited for the next tile's loads before every transposed V read).
+  __shared__ __attribute__((aligned(1024))) char k0_[TILE], v0_[TILE], k1_[TILE], v1_[TILE];
+  lds_t* const kst[2] = {lds_base(k0_), lds_base(k1_)};
+  lds_t* const vst[2] = {lds_base(v0_), lds_base(v1_)};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -98,8 +102,8 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
 
   const TileDma<D, BN, 4> kdma((const bf16_t*)a.k + hoff, N, wave, lane);
   const TileDma<D, BN, 4> vdma((const bf16_t*)a.v + hoff, N, wave, lane);
-  kdma.load(smem, 0);
-  vdma.load(smem + TILE, 0);
+  kdma.load(kst[0], 0);
+  vdma.load(vst[0], 0);
 
   // Q rows -> VGPRs, B-operand layout: lane holds query q, d = 16*ds + 8*hi .. +7.
   bf16x8 qr[DS];
@@ -121,12 +125,12 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   auto tile_step = [&](int j, const int ST) {
     const int n0 = j * BN;
     if (j + 1 < nt) {
-      kdma.load(smem + (ST ^ 1) * STAGE, n0 + BN);
-      vdma.load(smem + (ST ^ 1) * STAGE + TILE, n0 + BN);
+      kdma.load(kst[ST ^ 1], n0 + BN);
+      vdma.load(vst[ST ^ 1], n0 + BN);
     }
     if (j < wnt) {
-      const lds_t* kt = smem + ST * STAGE;
-      const lds_t* vt = kt + TILE;
+      const lds_t* kt = kst[ST];
+      const lds_t* vt = vst[ST];
       // S^T (64 keys x 32 queries) as two 32x32 blocks.
       f32x16 s0 = mfma32x32x16_z(row_operand<D>(kt, 0, 0, lane), qr[0]);
       f32x16 s1 = mfma32x32x16_z(row_operand<D>(kt, 32, 0, lane), qr[0]);
@@ -134,6 +138,13 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
       for (int ds = 1; ds < DS; ++ds) {
         s0 = mfma32x32x16(row_operand<D>(kt, 0, ds * 2, lane), qr[ds], s0);
         s1 = mfma32x32x16(row_operand<D>(kt, 32, ds * 2, lane), qr[ds], s1);
+      }
+      // Keep several K operand reads in flight ahead of the score MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * DS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 2 * DS - 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       // Key n0 + hi*4 + c (c = (i/4)*8 + i%4, +32 for s1) is visible iff c <= lim.
       if (n0 + BN > L || (CAUSAL && n0 + BN - 1 > qw)) {
@@ -179,6 +190,13 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           o[db] = mfma32x32x16(tr_operand<D>(vt, ks * 16, db * 32, lane), pb[ks], o[db]);
+      // Transposed V reads: eight in flight ahead of the P V MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (i < 4 * DB - 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
     }
     dma_wait();
     __syncthreads();
@@ -318,18 +336,10 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int BM = 128, BN = 64;
-  constexpr int lds = 2 * 2 * BN * D * 2;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)fwd_bf16_kernel<D, CAUSAL>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  constexpr int BM = 128;
   const int nm = (a.N + BM - 1) / BM;
   dim3 grid((unsigned)(nm * a.B * a.H)), block(256);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), grid, block, lds, stream, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -4,21 +4,21 @@
 namespace attn {
 
 // MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each
-// with a private L2. When the head count is a multiple of 8 the mapping keeps
-// every tile of one (batch, head) on one XCD, so that head's K/V tiles are
-// fetched from HBM into that XCD's L2 and reused there by all its row tiles.
-// Within an XCD the heads are visited one after another; with heavy_first
-// (causal masks) each head's tiles go from the last row tile (most KV tiles
-// to visit) to the first, so the longest workgroups start earliest and the
-// launch ends on short ones.
+// with a private L2. Workgroups are ordered by row tile first: with
+// heavy_first (causal masks, where the last row tiles visit the most KV
+// tiles) every head's heaviest tile is launched before any lighter one, so
+// the longest workgroups start earliest and the launch ends on short ones.
+// Within one row tile the heads are split over the XCDs: when the head count
+// is a multiple of 8, workgroup b runs on XCD b % 8 and only ever touches
+// heads xcd*H/8 .. xcd*H/8 + H/8 - 1, so each head's K/V is cached in one L2.
 __host__ __device__ inline void tile_order(int block, int num_tiles, int num_heads,
                                            bool heavy_first, int& head, int& tile) {
   int r;
   if ((num_heads & 7) == 0) {
     const int xcd = block & 7, slot = block >> 3;
     const int heads_per_xcd = num_heads >> 3;
-    head = xcd * heads_per_xcd + slot / num_tiles;
-    r = slot % num_tiles;
+    head = xcd * heads_per_xcd + slot % heads_per_xcd;
+    r = slot / heads_per_xcd;
   } else {
     head = block % num_heads;
     r = block / num_heads;
