@@ -95,6 +95,49 @@ def copy_calibration(torch, steps):
                       "bytes_written_per_launch": COPY_BYTES, "launches": steps}), flush=True)
 
 
+BWD_WORKLOAD = "causal_fwdbwd_bf16_b2_h16_n8192_d128"
+
+
+def bench_backward(torch, ea, steps, warmup=3):
+    """Time the recompute backward (delta, dK/dV and dQ kernels) on the causal
+    B=2 H=16 N=8192 d=128 workload, with O and LSE from one forward pass.
+    FLOPs follow the 5-GEMM convention, 10*B*H*N^2*d halved for causal; the
+    kernels execute 7 GEMMs' worth (S and dP are recomputed for dQ)."""
+    from attn_inputs import WORKLOADS, make_workload_inputs
+    w = WORKLOADS[BWD_WORKLOAD]
+    x = make_workload_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = ea.attn_fwd(q, k, v, scale=w.scale, causal=w.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ea.attn_bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
+                    workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(per) / len(per)
+    flops = 10.0 * w.B * w.H * w.N * w.N * w.d / 2
+    executed = 14.0 * w.B * w.H * w.N * w.N * w.d / 2
+    return {"workload": BWD_WORKLOAD, "ms_mean": round(mean_ms, 4), "ms_median": round(per[len(per) // 2], 4),
+            "tflops": round(flops / (mean_ms * 1e-3) / 1e12, 2),
+            "tflops_executed": round(executed / (mean_ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(flops / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "flop_convention": "10*B*H*N^2*d/2 (5 GEMMs, causal half); executed = 14*B*H*N^2*d/2"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,7 +145,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 disables it)")
-    ap.add_argument("--mode", choices=["fwd", "copy"], default="fwd",
+    ap.add_argument("--bwd-steps", type=int, default=10,
+                    help="timed backward passes on the causal B=2 H=16 N=8192 d=128 workload "
+                         "(reported under \"bwd\"; 0 skips them)")
+    ap.add_argument("--mode", choices=["fwd", "bwd", "copy"], default="fwd",
                     help="fwd: the benchmark; copy: a plain device copy of known size, whose "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the traffic figure")
     args = ap.parse_args()
@@ -116,6 +162,9 @@ def main():
         copy_calibration(torch, args.steps)
         return
     import exact_attention_24_amd as ea
+    if args.mode == "bwd":
+        print(json.dumps({"mode": "bwd", **bench_backward(torch, ea, args.steps, args.warmup)}), flush=True)
+        return
     from attn_inputs import WORKLOADS, make_workload_inputs
 
     w = WORKLOADS[WORKLOAD]
@@ -175,6 +224,8 @@ def main():
                      "kernel": "fwd_bf16_kernel<128, causal>",
                      "algorithmic": "4*B*H*N^2*d/2 FLOP per launch"},
     }
+    if args.bwd_steps > 0:
+        out["bwd"] = bench_backward(torch, ea, args.bwd_steps)
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(x, w, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -106,4 +106,12 @@ struct TileDma {
 // Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0).
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N of this wave's most recent vector-memory loads are
+// still in flight (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void dma_wait_allbut() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 }  // namespace attn
