@@ -35,6 +35,11 @@ attn_status check_sizes(int B, int H, int N, int d, attn_dtype dtype) {
 
 bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
 
+size_t attn_bwd_section_bytes(int B, int H, int N) {
+  const size_t rows = (size_t)B * H * N;
+  return ((rows * sizeof(float) + 255) / 256) * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,8 +84,8 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype dtype) {
   if (check_sizes(B, H, N, d, dtype) != ATTN_OK) return 0;
-  const size_t rows = (size_t)B * H * N;
-  return ((rows * sizeof(float) + 255) / 256) * 256;
+  // delta and log2-scaled LSE, one fp32 per row each, each section 256-byte aligned
+  return 2 * attn_bwd_section_bytes(B, H, N);
 }
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -104,6 +109,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.delta = (float*)workspace;
+  a.lse2 = (float*)((char*)workspace + attn_bwd_section_bytes(B, H, N));
   a.seqlens = seqlens;
   a.B = B; a.H = H; a.N = N;
   a.scale = scale;

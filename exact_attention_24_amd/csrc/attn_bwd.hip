@@ -15,11 +15,15 @@
 // With S = scale*Q K^T, dQ = scale*dS K and dK = scale*dS^T Q.
 //
 // Three launches on one stream:
-//   bwd_pre:  delta_i = rowsum(dO_i o O_i)                    (HBM-bound)
+//   bwd_pre:  delta_i = rowsum(dO_i o O_i) and LSE_i*log2(e)    (HBM-bound)
 //   bwd_dkdv: one workgroup per 128 keys; loops over the query tiles that can
 //             see those keys, accumulating dK and dV in registers
 //   bwd_dq:   one workgroup per 128 queries; loops over the key tiles they
 //             see, accumulating dQ in registers (no atomics: deterministic)
+// Tiles reach LDS through direct buffer->LDS loads into XOR-swizzled layouts,
+// one LDS array per stage and tensor, as in the forward kernel. Every load is
+// bounded by the sequence's valid length L, so padded positions are never
+// read: they enter the products as zeros.
 #include "attn_common.h"
 #include "attn_kernels.h"
 #include "attn_sched.h"
@@ -36,21 +40,57 @@ __device__ __forceinline__ int seq_len(const BwdArgs& a, int b) {
 }
 
 // Store a transposed 32-row accumulator block: lane holds column `row` of the
-// result and values for d = db*32 + g*8 + hi*4 + {0..3}.
+// result and values for d = db*32 + g*8 + hi*4 + {0..3}. A lane with
+// valid == false stores zeros (selected, so a non-finite accumulator in a
+// discarded lane cannot leak through a multiply by 0).
 template <int DB>
-__device__ __forceinline__ void store_rowT(bf16_t* rowp, const f32x16* acc, float mul, int hi) {
+__device__ __forceinline__ void store_rowT(bf16_t* rowp, const f32x16* acc, float mul, bool valid,
+                                           int hi) {
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const u32x2 w = {pack_bf16x2(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul),
-                       pack_bf16x2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+      const uint32_t w0 = pack_bf16x2(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul);
+      const uint32_t w1 = pack_bf16x2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
+      const u32x2 w = {valid ? w0 : 0u, valid ? w1 : 0u};
       gstore8(rowp + db * 32 + g * 8 + hi * 4, w);
     }
 }
 
+// Per-lane LDS byte offsets of the MFMA operands of a swizzled [rows][D] tile,
+// computed once per kernel (the swizzle depends on the row modulo 16 only):
+//   row[ds]    A operand, row lane%32 (+ row0, a multiple of 32), chunk 2ds + lane/32
+//   tr[db][h]  transposed operand (see tr_operand) at column db*32, rows
+//              8h + 4*(lane/32) + (lane&15)/4 (+ row0, a multiple of 16)
+template <int D>
+struct TileAddr {
+  static constexpr int DS = D / 16, DB = D / 32;
+  int row[DS];
+  int tr[DB][2];
+  __device__ __forceinline__ explicit TileAddr(int lane) {
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) row[ds] = tile_off<D>(lane & 31, ds * 2 + (lane >> 5));
+    const int r = (lane >> 5) * 4 + ((lane & 15) >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = db * 32 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+      tr[db][0] = tile_off_col<D>(r, col);
+      tr[db][1] = tile_off_col<D>(r + 8, col);
+    }
+  }
+  __device__ __forceinline__ bf16x8 rowop(const lds_t* t, int row0, int ds) const {
+    return as_bf16x8(lds_load16(t + row[ds] + row0 * (D * 2)));
+  }
+  __device__ __forceinline__ bf16x8 trop(const lds_t* t, int row0, int db) const {
+    const u32x2 lo = lds_load_tr16(t + tr[db][0] + row0 * (D * 2));
+    const u32x2 up = lds_load_tr16(t + tr[db][1] + row0 * (D * 2));
+    return join_bf16x8(lo, up);
+  }
+};
+
 // ---------------------------------------------------------------------------
-// delta_i = sum_d dO_i[d] * O_i[d] in fp32; 0 for padded rows.
+// delta_i = sum_d dO_i[d] * O_i[d] in fp32 and lse2_i = LSE_i * log2(e);
+// both 0 for padded rows.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a) {
@@ -74,14 +114,17 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, TPR);
-  if (row < total && c == 0) a.delta[row] = valid ? part : 0.f;
+  if (row < total && c == 0) {
+    a.delta[row] = valid ? part : 0.f;
+    a.lse2[row] = valid ? a.lse[row] * kLog2e : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV: workgroup = 4 waves x 32 keys. Each wave keeps its K and V rows in
 // VGPRs (B operands of S = Q K^T and dP = dO V^T) and accumulates dK^T, dV^T.
-// Query tiles of 64 rows (Q, dO, log2-scaled LSE, delta) are double-buffered in
-// LDS and processed as two 32-row sub-blocks:
+// Query tiles of 64 rows (Q, dO, and the rows' lse2 and delta) are
+// double-buffered in LDS and processed as two 32-row sub-blocks:
 //   S  (q x key)   = Q  K^T        A = Q rows (LDS),   B = K (VGPR)
 //   P              = exp2(S*scale*log2e - LSE*log2e), masked
 //   dV^T (d x key) += dO^T P       A = dO^T (transposing LDS read), B = P
@@ -90,17 +133,17 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a) {
 //   dK^T (d x key) += Q^T dS       A = Q^T (transposing LDS read),  B = dS
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   constexpr int BN = 128, BM = 64;
   constexpr int TILE = BM * D * 2;
-  constexpr int STAGE = 2 * TILE + 2 * BM * 4;
-  constexpr int CH = D / 8, LOADS = BM * CH / 256;
+  constexpr int CH = D / 8;
   constexpr int DS = D / 16, DB = D / 32;
 
-  extern __shared__ __attribute__((aligned(16))) char smem_generic[];
-  lds_t* smem = lds_base(smem_generic);
+  __shared__ __attribute__((aligned(1024))) char q0_[TILE], q1_[TILE], o0_[TILE], o1_[TILE];
+  __shared__ __attribute__((aligned(256))) char st0_[2 * BM * 4], st1_[2 * BM * 4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int N = a.N;
   const int nkt = (N + BN - 1) / BN;
@@ -109,12 +152,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
   const int L = seq_len(a, bh / a.H);
   const int n0 = kt * BN;
   const size_t hoff = (size_t)bh * N * D;
-  const bf16_t* __restrict__ Qh = (const bf16_t*)a.q + hoff;
   const bf16_t* __restrict__ Kh = (const bf16_t*)a.k + hoff;
   const bf16_t* __restrict__ Vh = (const bf16_t*)a.v + hoff;
-  const bf16_t* __restrict__ dOh = (const bf16_t*)a.dO + hoff;
-  const float* __restrict__ lse_h = a.lse + (size_t)bh * N;
-  const float* __restrict__ del_h = a.delta + (size_t)bh * N;
   bf16_t* __restrict__ dKh = (bf16_t*)a.dk + hoff;
   bf16_t* __restrict__ dVh = (bf16_t*)a.dv + hoff;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -131,46 +170,36 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
 
   const int kw = n0 + wave * 32;  // first key of this wave
   const int key = kw + l32;       // this lane's key (B-operand column)
+  const int q_begin = CAUSAL ? (n0 / BM) * BM : 0;
+  // Query tiles are taken in pairs (one per LDS stage); an odd count gets one
+  // more tile past L, which loads as zeros and is fully masked.
+  const int nqt = ((L - q_begin + BM - 1) / BM + 1) & ~1;
+  const float c2 = a.scale_log2;
+
+  const TileDma<D, BM, 4> qdma((const bf16_t*)a.q + hoff, L, wave, lane);
+  const TileDma<D, BM, 4> odma((const bf16_t*)a.dO + hoff, L, wave, lane);
+  const float* lse2_h = a.lse2 + (size_t)bh * N;
+  const float* delta_h = a.delta + (size_t)bh * N;
+  // Stage st: Q tile, dO tile, then lse2[BM] and delta[BM] of the same rows.
+  auto load_tile = [&](int q0, int st) {
+    qdma.load(lds_base(st ? q1_ : q0_), q0);
+    odma.load(lds_base(st ? o1_ : o0_), q0);
+    lds_t* stats = lds_base(st ? st1_ : st0_);
+    if (wave == 0)
+      vec64_dma(stats, lse2_h, L, q0, lane);
+    else if (wave == 1)
+      vec64_dma(stats + BM * 4, delta_h, L, q0, lane);
+  };
+  load_tile(q_begin, 0);
+
   bf16x8 kreg[DS], vreg[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds) {
     const size_t off = (size_t)key * D + ds * 16 + hi * 8;
-    kreg[ds] = as_bf16x8(key < N ? gload16(Kh + off) : zero4);
-    vreg[ds] = as_bf16x8(key < N ? gload16(Vh + off) : zero4);
+    kreg[ds] = as_bf16x8(key < L ? gload16(Kh + off) : zero4);
+    vreg[ds] = as_bf16x8(key < L ? gload16(Vh + off) : zero4);
   }
-
-  const int q_begin = CAUSAL ? (n0 / BM) * BM : 0;
-  const int nqt = (L - q_begin + BM - 1) / BM;
-  const float c2 = a.scale_log2;
-
-  u32x4 qr[LOADS], dor[LOADS];
-  float lr = 0.f, dr = 0.f;
-  auto gload_tile = [&](int q0) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i, row = c / CH, col = c % CH, g = q0 + row;
-      qr[i] = g < N ? gload16(Qh + (size_t)g * D + col * 8) : zero4;
-      dor[i] = g < N ? gload16(dOh + (size_t)g * D + col * 8) : zero4;
-    }
-    if (tid < BM) {
-      const int g = q0 + tid;
-      lr = g < L ? lse_h[g] * kLog2e : 0.f;
-      dr = g < L ? del_h[g] : 0.f;
-    }
-  };
-  auto lds_store_tile = [&](int st) {
-    lds_t* qt = smem + st * STAGE;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i, row = c / CH, col = c % CH;
-      lds_store16(qt + tile_off<D>(row, col), qr[i]);
-      lds_store16(qt + TILE + tile_off<D>(row, col), dor[i]);
-    }
-    if (tid < BM) {
-      lds_storef(qt + 2 * TILE + tid * 4, lr);
-      lds_storef(qt + 2 * TILE + BM * 4 + tid * 4, dr);
-    }
-  };
+  const TileAddr<D> ad(lane);
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -178,32 +207,31 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { dk[db][i] = 0.f; dv[db][i] = 0.f; }
 
-  gload_tile(q_begin);
-  lds_store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < nqt; ++t) {
-    const int st = t & 1, qt0 = q_begin + t * BM;
-    if (t + 1 < nqt) gload_tile(qt0 + BM);
-    const lds_t* Qt = smem + st * STAGE;
-    const lds_t* dOt = Qt + TILE;
-    const lds_t* lse_t = Qt + 2 * TILE;
+  // MASKED is set for the two tiles on the causal diagonal only. Elsewhere no
+  // mask is needed: every key of the tile is visible to every query, and rows
+  // at or past L hold zeros (Q, dO, delta, lse2 all 0, so p = 1 and dS = 0)
+  // and add nothing to dK or dV; lanes whose key is at or past L are
+  // discarded at the store.
+  auto step = [&](int t, const int st, const bool MASKED) {
+    const int qt0 = q_begin + t * BM;
+    if (t + 1 < nqt) load_tile(qt0 + BM, st ^ 1);
+    const lds_t* Qt = lds_base(st ? q1_ : q0_);
+    const lds_t* dOt = lds_base(st ? o1_ : o0_);
+    const lds_t* lse_t = lds_base(st ? st1_ : st0_);
     const lds_t* del_t = lse_t + BM * 4;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const int qs = qt0 + sb * 32;
-      if (kw >= L || qs >= L || (CAUSAL && qs + 31 < kw)) continue;
-      f32x16 s, dp;
+      f32x16 s = mfma32x32x16_z(ad.rowop(Qt, sb * 32, 0), kreg[0]);
+      f32x16 dp = mfma32x32x16_z(ad.rowop(dOt, sb * 32, 0), vreg[0]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const bf16x8 qa = as_bf16x8(lds_load16(Qt + tile_off<D>(sb * 32 + l32, ds * 2 + hi)));
-        const bf16x8 da = as_bf16x8(lds_load16(dOt + tile_off<D>(sb * 32 + l32, ds * 2 + hi)));
-        s = mfma32x32x16(qa, kreg[ds], s);
-        dp = mfma32x32x16(da, vreg[ds], dp);
+      for (int ds = 1; ds < DS; ++ds) {
+        s = mfma32x32x16(ad.rowop(Qt, sb * 32, ds), kreg[ds], s);
+        dp = mfma32x32x16(ad.rowop(dOt, sb * 32, ds), vreg[ds], dp);
       }
-      const bool need_mask = qs + 32 > L || kw + 32 > L || (CAUSAL && qs < kw + 31);
+      // Accumulator element i is query qs + hi*4 + c (c = (i/4)*8 + i%4) against
+      // this lane's key; causally visible iff c >= lo.
+      const int lo = key - qs - hi * 4;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int rl = sb * 32 + g * 8 + hi * 4;  // first of 4 consecutive query rows
@@ -213,10 +241,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g + e;
           float p = fast_exp2(fmaf(s[i], c2, -l4[e]));
-          if (need_mask) {
-            const int q = qt0 + rl + e;
-            if (key >= L || q >= L || (CAUSAL && key > q)) p = 0.f;
-          }
+          if (MASKED) p = (g * 8 + e >= lo) ? p : 0.f;
           s[i] = p;
           dp[i] = p * (dp[i] - d4[e]);
         }
@@ -227,18 +252,31 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
         const bf16x8 sb16 = pack8(dp, h);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dv[db] = mfma32x32x16(tr_operand<D>(dOt, sb * 32 + h * 16, db * 32, lane), pb, dv[db]);
-          dk[db] = mfma32x32x16(tr_operand<D>(Qt, sb * 32 + h * 16, db * 32, lane), sb16, dk[db]);
+          dv[db] = mfma32x32x16(ad.trop(dOt, sb * 32 + h * 16, db), pb, dv[db]);
+          dk[db] = mfma32x32x16(ad.trop(Qt, sb * 32 + h * 16, db), sb16, dk[db]);
         }
       }
     }
-    if (t + 1 < nqt) lds_store_tile(st ^ 1);
+    dma_wait();
     __syncthreads();
+  };
+
+  dma_wait();
+  __syncthreads();
+  int t = 0;
+  if (CAUSAL) {  // query tiles [n0, n0 + 128): the diagonal
+    step(0, 0, true);
+    step(1, 1, true);
+    t = 2;
+  }
+  for (; t < nqt; t += 2) {
+    step(t, 0, false);
+    step(t + 1, 1, false);
   }
 
   if (key < N) {
-    store_rowT<DB>(dKh + (size_t)key * D, dk, a.scale, hi);
-    store_rowT<DB>(dVh + (size_t)key * D, dv, 1.f, hi);
+    store_rowT<DB>(dKh + (size_t)key * D, dk, a.scale, key < L, hi);
+    store_rowT<DB>(dVh + (size_t)key * D, dv, 1.f, key < L, hi);
   }
 }
 
@@ -251,17 +289,16 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
 //   dQ^T (d x q)  += K^T dS^T  A = K^T (transposing LDS read), B = dS^T
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   constexpr int BM = 128, BN = 64;
   constexpr int TILE = BN * D * 2;
-  constexpr int STAGE = 2 * TILE;
-  constexpr int CH = D / 8, LOADS = BN * CH / 256;
+  constexpr int CH = D / 8;
   constexpr int DS = D / 16, DB = D / 32;
 
-  extern __shared__ __attribute__((aligned(16))) char smem_generic[];
-  lds_t* smem = lds_base(smem_generic);
+  __shared__ __attribute__((aligned(1024))) char k0_[TILE], v0_[TILE], k1_[TILE], v1_[TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int N = a.N;
   const int nm = (N + BM - 1) / BM;
@@ -271,8 +308,6 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
   const int m0 = mt * BM;
   const size_t hoff = (size_t)bh * N * D;
   const bf16_t* __restrict__ Qh = (const bf16_t*)a.q + hoff;
-  const bf16_t* __restrict__ Kh = (const bf16_t*)a.k + hoff;
-  const bf16_t* __restrict__ Vh = (const bf16_t*)a.v + hoff;
   const bf16_t* __restrict__ dOh = (const bf16_t*)a.dO + hoff;
   bf16_t* __restrict__ dQh = (bf16_t*)a.dq + hoff;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -286,40 +321,28 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
 
   const int qw = m0 + wave * 32, q = qw + l32;
   const bool qvalid = q < L;
-  const float lse2 = qvalid ? a.lse[(size_t)bh * N + q] * kLog2e : 0.f;
+  const int kv_end = CAUSAL ? min(L, m0 + BM) : L;
+  // Key tiles in pairs (one per LDS stage); an odd count gets one more tile,
+  // which is fully masked. Every wave computes every tile, also those past its
+  // own causal limit: the waves meet at a barrier every tile anyway.
+  const int nt = ((kv_end + BN - 1) / BN + 1) & ~1;
+  const float c2 = a.scale_log2;
+
+  const TileDma<D, BN, 4> kdma((const bf16_t*)a.k + hoff, L, wave, lane);
+  const TileDma<D, BN, 4> vdma((const bf16_t*)a.v + hoff, L, wave, lane);
+  kdma.load(lds_base(k0_), 0);
+  vdma.load(lds_base(v0_), 0);
+
+  const float lse2 = qvalid ? a.lse2[(size_t)bh * N + q] : 0.f;
   const float dq_delta = qvalid ? a.delta[(size_t)bh * N + q] : 0.f;
   bf16x8 qreg[DS], doreg[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds) {
     const size_t off = (size_t)q * D + ds * 16 + hi * 8;
-    qreg[ds] = as_bf16x8(q < N ? gload16(Qh + off) : zero4);
-    doreg[ds] = as_bf16x8(q < N ? gload16(dOh + off) : zero4);
+    qreg[ds] = as_bf16x8(qvalid ? gload16(Qh + off) : zero4);
+    doreg[ds] = as_bf16x8(qvalid ? gload16(dOh + off) : zero4);
   }
-
-  const int kv_end = CAUSAL ? min(L, m0 + BM) : L;
-  const int nt = (kv_end + BN - 1) / BN;
-  const int w_end = (qw >= L) ? 0 : (CAUSAL ? min(L, qw + 32) : L);
-  const int wnt = (w_end + BN - 1) / BN;
-  const float c2 = a.scale_log2;
-
-  u32x4 kr[LOADS], vr[LOADS];
-  auto gload_tile = [&](int n0) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i, row = c / CH, col = c % CH, g = n0 + row;
-      kr[i] = g < N ? gload16(Kh + (size_t)g * D + col * 8) : zero4;
-      vr[i] = g < N ? gload16(Vh + (size_t)g * D + col * 8) : zero4;
-    }
-  };
-  auto lds_store_tile = [&](int st) {
-    lds_t* kt = smem + st * STAGE;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + 256 * i, row = c / CH, col = c % CH;
-      lds_store16(kt + tile_off<D>(row, col), kr[i]);
-      lds_store16(kt + TILE + tile_off<D>(row, col), vr[i]);
-    }
-  };
+  const TileAddr<D> ad(lane);
 
   f32x16 acc[DB];
 #pragma unroll
@@ -327,69 +350,75 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  gload_tile(0);
-  lds_store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < nt; ++j) {
-    const int st = j & 1, n0 = j * BN;
-    if (j + 1 < nt) gload_tile(n0 + BN);
-    if (j < wnt) {
-      const lds_t* Kt = smem + st * STAGE;
-      const lds_t* Vt = Kt + TILE;
-      const bool need_mask = n0 + BN > L || qw + 32 > L || (CAUSAL && n0 + BN - 1 > qw);
-      // One 32-key block at a time keeps only one S^T and one dP^T block live.
+  // MASKED is set for the last pair of key tiles only: it holds the causal
+  // diagonal and any keys at or past L. In every earlier tile all keys are
+  // below L and, with a causal mask, below m0, so all are visible. Lanes whose
+  // query is at or past L compute on zero rows and are discarded at the store.
+  auto step = [&](int j, const int st, const bool MASKED) {
+    const int n0 = j * BN;
+    if (j + 1 < nt) {
+      kdma.load(lds_base(st ? k0_ : k1_), n0 + BN);
+      vdma.load(lds_base(st ? v0_ : v1_), n0 + BN);
+    }
+    const lds_t* Kt = lds_base(st ? k1_ : k0_);
+    const lds_t* Vt = lds_base(st ? v1_ : v0_);
+    // One 32-key block at a time keeps only one S^T and one dP^T block live.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 s, dp;
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = mfma32x32x16_z(ad.rowop(Kt, kb * 32, 0), qreg[0]);
+      f32x16 dp = mfma32x32x16_z(ad.rowop(Vt, kb * 32, 0), doreg[0]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
+      for (int ds = 1; ds < DS; ++ds) {
+        s = mfma32x32x16(ad.rowop(Kt, kb * 32, ds), qreg[ds], s);
+        dp = mfma32x32x16(ad.rowop(Vt, kb * 32, ds), doreg[ds], dp);
+      }
+      // Element i is key n0 + kb*32 + hi*4 + c (c = (i/4)*8 + i%4) against this
+      // lane's query; it is visible iff c <= lim.
+      const int lim = (CAUSAL ? min(q, L - 1) : L - 1) - n0 - kb * 32 - hi * 4;
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-          const bf16x8 ka = as_bf16x8(lds_load16(Kt + tile_off<D>(kb * 32 + l32, ds * 2 + hi)));
-          const bf16x8 va = as_bf16x8(lds_load16(Vt + tile_off<D>(kb * 32 + l32, ds * 2 + hi)));
-          s = mfma32x32x16(ka, qreg[ds], s);
-          dp = mfma32x32x16(va, doreg[ds], dp);
-        }
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(s[i], c2, -lse2));
+        if (MASKED) p = ((i >> 2) * 8 + (i & 3)) <= lim ? p : 0.f;
+        dp[i] = p * (dp[i] - dq_delta);
+      }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(fmaf(s[i], c2, -lse2));
-          if (need_mask) {
-            const int key = n0 + kb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-            if (key >= L || !qvalid || (CAUSAL && key > q)) p = 0.f;
-          }
-          dp[i] = p * (dp[i] - dq_delta);
-        }
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 dsb = pack8(dp, h);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const bf16x8 dsb = pack8(dp, h);
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            acc[db] = mfma32x32x16(tr_operand<D>(Kt, kb * 32 + h * 16, db * 32, lane), dsb, acc[db]);
-        }
+        for (int db = 0; db < DB; ++db)
+          acc[db] = mfma32x32x16(ad.trop(Kt, kb * 32 + h * 16, db), dsb, acc[db]);
       }
     }
-    if (j + 1 < nt) lds_store_tile(st ^ 1);
+    dma_wait();
     __syncthreads();
-  }
+  };
 
-  if (q < N) store_rowT<DB>(dQh + (size_t)q * D, acc, qvalid ? a.scale : 0.f, hi);
+  dma_wait();
+  __syncthreads();
+  int j = 0;
+  for (; j < nt - 2; j += 2) {
+    step(j, 0, false);
+    step(j + 1, 1, false);
+  }
+  step(j, 0, true);
+  step(j + 1, 1, true);
+
+  if (q < N) store_rowT<DB>(dQh + (size_t)q * D, acc, a.scale, qvalid, hi);
+}
+
+// Thin __global__ wrappers: with the buffer builtins inside a __global__
+// template body, the host pass dropped some of the launch stubs.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
+  bwd_dkdv_body<D, CAUSAL>(a);
+}
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
+  bwd_dq_body<D, CAUSAL>(a);
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  constexpr int lds_dkdv = 2 * (2 * 64 * D * 2 + 2 * 64 * 4);
-  constexpr int lds_dq = 2 * (2 * 64 * D * 2);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, CAUSAL>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_dkdv);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)bwd_dq_kernel<D, CAUSAL>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds_dq);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const long long rows = (long long)a.B * a.H * a.N;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
@@ -398,11 +427,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int heads = a.B * a.H;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(heads * ((a.N + 127) / 128))),
-                     dim3(256), lds_dkdv, stream, a);
+                     dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(heads * ((a.N + 127) / 128))),
-                     dim3(256), lds_dq, stream, a);
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -63,15 +63,16 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int h) {
 }
 
 // Direct global -> LDS tile loads (buffer_load_dwordx4 ... lds) for one
-// (batch, head). The buffer resource spans exactly the head's N x D elements,
-// so rows past the end read as zeros (hardware range check): the tile never
-// holds stale LDS bytes that could be NaN bit patterns, and no clamping is
-// needed. NWAVES waves share a tile of ROWS rows; the calling wave fills the
-// 1 KB row groups g = wave, wave + NWAVES, ... (64/(D/8) rows each), lane l
-// writing physical chunk l % (D/8) of row l / (D/8), i.e. logical chunk
+// (batch, head). Each load builds a buffer resource whose base is the tile's
+// first row and whose range ends at row n_rows, so rows at or past n_rows read
+// as zeros (hardware range check on the per-lane offset; the scalar offset is
+// left at 0): the tile never holds stale LDS bytes that could be NaN bit
+// patterns, rows past the end are never fetched, and no clamping is needed.
+// NWAVES waves share a tile of ROWS rows; the calling wave fills the 1 KB row
+// groups g = wave, wave + NWAVES, ... (64/(D/8) rows each), lane l writing
+// physical chunk l % (D/8) of row l / (D/8), i.e. logical chunk
 // (l % (D/8)) ^ swz(row). The per-lane byte offsets do not depend on which
-// tile is loaded, so they are computed once; the tile's first row enters as a
-// scalar offset.
+// tile is loaded, so they are computed once.
 template <int D, int ROWS, int NWAVES>
 struct TileDma {
   static constexpr int CPR = D / 8;      // 16-byte chunks per row
@@ -79,13 +80,15 @@ struct TileDma {
   static constexpr int ITER = ROWS / RPG / NWAVES;
   static_assert(ITER * RPG * NWAVES == ROWS, "tile rows must split evenly over the waves");
 
-  __amdgpu_buffer_rsrc_t rsrc;
+  const bf16_t* head;
+  int n_rows;
   uint32_t voff[ITER];
   int wave;
 
-  __device__ __forceinline__ TileDma(const bf16_t* head, int n_rows, int wave_, int lane) {
+  __device__ __forceinline__ TileDma(const bf16_t* head_, int n_rows_, int wave_, int lane) {
+    head = head_;
+    n_rows = n_rows_;
     wave = wave_;
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)head, (short)0, n_rows * D * 2, 0x00020000);
     const int rsub = lane / CPR, pc = lane % CPR;
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
@@ -95,13 +98,26 @@ struct TileDma {
   }
   // Enqueue the loads of rows [row0, row0 + ROWS) into `tile`.
   __device__ __forceinline__ void load(lds_t* tile, int row0) const {
-    const uint32_t soff = (uint32_t)row0 * (D * 2);
+    const uint32_t bytes = (uint32_t)max(n_rows - row0, 0) * (uint32_t)(D * 2);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(head + (size_t)row0 * D), (short)0, (int)bytes, 0x00020000);
 #pragma unroll
     for (int it = 0; it < ITER; ++it)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (ATTN_LDS void*)(tile + (wave + it * NWAVES) * 1024), 16, voff[it], soff, 0, 0);
+          rsrc, (ATTN_LDS void*)(tile + (wave + it * NWAVES) * 1024), 16, voff[it], 0, 0, 0);
   }
 };
+
+// One 4-byte value per lane, 64 lanes, straight into LDS: values
+// [row0, row0 + 64) of an fp32 array of n_rows entries (zeros at or past
+// n_rows), written to lds[0 .. 256).
+__device__ __forceinline__ void vec64_dma(lds_t* lds, const float* base, int n_rows, int row0,
+                                          int lane) {
+  const uint32_t bytes = (uint32_t)max(n_rows - row0, 0) * 4u;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0), (short)0, (int)bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (ATTN_LDS void*)lds, 4, lane * 4, 0, 0, 0);
+}
 
 // Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0).
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -100,8 +100,9 @@ def test_bwd_rejects_bad_arguments(L, kw, want):
 
 
 def test_workspace_bytes(L):
-    assert L.attn_bwd_workspace_bytes(2, 16, 8192, 128, 1) == 2 * 16 * 8192 * 4
-    assert L.attn_bwd_workspace_bytes(1, 1, 3, 64, 1) == 256  # rounded up to 256 bytes
+    # two fp32 [B,H,N] sections (delta, log2-scaled LSE), each rounded up to 256 bytes
+    assert L.attn_bwd_workspace_bytes(2, 16, 8192, 128, 1) == 2 * (2 * 16 * 8192 * 4)
+    assert L.attn_bwd_workspace_bytes(1, 1, 3, 64, 1) == 2 * 256
     assert L.attn_bwd_workspace_bytes(1, 1, 0, 64, 1) == 0
     assert L.attn_bwd_workspace_bytes(1, 1, 8, 100, 1) == 0
 
