@@ -181,14 +181,13 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   const float* lse2_h = a.lse2 + (size_t)bh * N;
   const float* delta_h = a.delta + (size_t)bh * N;
   // Stage st: Q tile, dO tile, then lse2[BM] and delta[BM] of the same rows.
+  // Waves 0 and 2 both fetch lse2 and waves 1 and 3 both fetch delta (the
+  // same bytes to the same place), which keeps the code free of branches.
   auto load_tile = [&](int q0, int st) {
     qdma.load(lds_base(st ? q1_ : q0_), q0);
     odma.load(lds_base(st ? o1_ : o0_), q0);
-    lds_t* stats = lds_base(st ? st1_ : st0_);
-    if (wave == 0)
-      vec64_dma(stats, lse2_h, L, q0, lane);
-    else if (wave == 1)
-      vec64_dma(stats + BM * 4, delta_h, L, q0, lane);
+    const int odd = wave & 1;
+    vec64_dma(lds_base(st ? st1_ : st0_) + odd * (BM * 4), odd ? delta_h : lse2_h, L, q0, lane);
   };
   load_tile(q_begin, 0);
 
@@ -212,51 +211,136 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   // at or past L hold zeros (Q, dO, delta, lse2 all 0, so p = 1 and dS = 0)
   // and add nothing to dK or dV; lanes whose key is at or past L are
   // discarded at the store.
+  // The next tile's loads are issued first (past the end they read zeros and
+  // touch no memory), so the tile body is a single basic block.
   auto step = [&](int t, const int st, const bool MASKED) {
     const int qt0 = q_begin + t * BM;
-    if (t + 1 < nqt) load_tile(qt0 + BM, st ^ 1);
+    load_tile(qt0 + BM, st ^ 1);
     const lds_t* Qt = lds_base(st ? q1_ : q0_);
     const lds_t* dOt = lds_base(st ? o1_ : o0_);
     const lds_t* lse_t = lds_base(st ? st1_ : st0_);
     const lds_t* del_t = lse_t + BM * 4;
+
+    // Exponentials and dS of sub-block sb; also packs P and dS to bf16.
+    auto softmax_grad = [&](int sb, f32x16& s, f32x16& dp, const f32x4* l4, const f32x4* d4,
+                            bf16x8* pb, bf16x8* gb) {
+      // Element i is query qt0 + sb*32 + hi*4 + c (c = (i/4)*8 + i%4) against this
+      // lane's key; causally visible iff c >= lo.
+      const int lo = key - (qt0 + sb * 32) - hi * 4;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int qs = qt0 + sb * 32;
-      f32x16 s = mfma32x32x16_z(ad.rowop(Qt, sb * 32, 0), kreg[0]);
-      f32x16 dp = mfma32x32x16_z(ad.rowop(dOt, sb * 32, 0), vreg[0]);
-#pragma unroll
-      for (int ds = 1; ds < DS; ++ds) {
-        s = mfma32x32x16(ad.rowop(Qt, sb * 32, ds), kreg[ds], s);
-        dp = mfma32x32x16(ad.rowop(dOt, sb * 32, ds), vreg[ds], dp);
-      }
-      // Accumulator element i is query qs + hi*4 + c (c = (i/4)*8 + i%4) against
-      // this lane's key; causally visible iff c >= lo.
-      const int lo = key - qs - hi * 4;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rl = sb * 32 + g * 8 + hi * 4;  // first of 4 consecutive query rows
-        const f32x4 l4 = *(const ATTN_LDS f32x4*)(lse_t + rl * 4);
-        const f32x4 d4 = *(const ATTN_LDS f32x4*)(del_t + rl * 4);
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g + e;
-          float p = fast_exp2(fmaf(s[i], c2, -l4[e]));
+          float p = fast_exp2(fmaf(s[i], c2, -l4[g][e]));
           if (MASKED) p = (g * 8 + e >= lo) ? p : 0.f;
           s[i] = p;
-          dp[i] = p * (dp[i] - d4[e]);
+          dp[i] = p * (dp[i] - d4[g][e]);
         }
-      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const bf16x8 pb = pack8(s, h);
-        const bf16x8 sb16 = pack8(dp, h);
+        pb[h] = pack8(s, h);
+        gb[h] = pack8(dp, h);
+      }
+    };
+    auto read_stats = [&](int sb, f32x4* l4, f32x4* d4) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int rl = sb * 32 + g * 8 + hi * 4;  // first of 4 consecutive query rows
+        l4[g] = *(const ATTN_LDS f32x4*)(lse_t + rl * 4);
+        d4[g] = *(const ATTN_LDS f32x4*)(del_t + rl * 4);
+      }
+    };
+    auto read_tr = [&](int sb, bf16x8 (*qo)[2]) {  // qo[h*DB + db] = {dO^T, Q^T}
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dv[db] = mfma32x32x16(ad.trop(dOt, sb * 32 + h * 16, db), pb, dv[db]);
-          dk[db] = mfma32x32x16(ad.trop(Qt, sb * 32 + h * 16, db), sb16, dk[db]);
+          qo[h * DB + db][0] = ad.trop(dOt, sb * 32 + h * 16, db);
+          qo[h * DB + db][1] = ad.trop(Qt, sb * 32 + h * 16, db);
         }
-      }
+    };
+    auto grad_mfma = [&](bf16x8 (*qo)[2], const bf16x8* pb, const bf16x8* gb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = mfma32x32x16(qo[h * DB + db][0], pb[h], dv[db]);
+          dk[db] = mfma32x32x16(qo[h * DB + db][1], gb[h], dk[db]);
+        }
+    };
+
+    // The tile is two 32-query sub-blocks A (rows 0-31) and B (rows 32-63),
+    // laid out in phases separated by scheduling fences so that the exp/VALU
+    // work of one sub-block runs under the MFMAs of the other and every LDS
+    // read is issued a phase ahead of the MFMA that consumes it.
+    constexpr int PM = 2 * DS;  // MFMAs per phase
+    // Phase 1a: Q/dO row operands of A.
+    bf16x8 qa[DS], oa[DS];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      qa[ds] = ad.rowop(Qt, 0, ds);
+      oa[ds] = ad.rowop(dOt, 0, ds);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase 1b: S_A = Q_A K^T, dP_A = dO_A V^T; reads: row operands of B, stats of A.
+    f32x16 sA = mfma32x32x16_z(qa[0], kreg[0]);
+    f32x16 dpA = mfma32x32x16_z(oa[0], vreg[0]);
+#pragma unroll
+    for (int ds = 1; ds < DS; ++ds) {
+      sA = mfma32x32x16(qa[ds], kreg[ds], sA);
+      dpA = mfma32x32x16(oa[ds], vreg[ds], dpA);
+    }
+    bf16x8 qb[DS], ob[DS];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      qb[ds] = ad.rowop(Qt, 32, ds);
+      ob[ds] = ad.rowop(dOt, 32, ds);
+    }
+    f32x4 lA[4], dA[4];
+    read_stats(0, lA, dA);
+#pragma unroll
+    for (int i = 0; i < PM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase 2: S_B, dP_B; VALU of A; reads: stats of B, transposed operands of A.
+    f32x16 sB = mfma32x32x16_z(qb[0], kreg[0]);
+    f32x16 dpB = mfma32x32x16_z(ob[0], vreg[0]);
+#pragma unroll
+    for (int ds = 1; ds < DS; ++ds) {
+      sB = mfma32x32x16(qb[ds], kreg[ds], sB);
+      dpB = mfma32x32x16(ob[ds], vreg[ds], dpB);
+    }
+    bf16x8 pA[2], gA[2];
+    softmax_grad(0, sA, dpA, lA, dA, pA, gA);
+    f32x4 lB[4], dB[4];
+    read_stats(1, lB, dB);
+    bf16x8 trA[2 * DB][2];
+    read_tr(0, trA);
+#pragma unroll
+    for (int i = 0; i < PM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase 3: dV, dK += sub-block A; VALU of B; reads: transposed operands of B.
+    grad_mfma(trA, pA, gA);
+    bf16x8 pB[2], gB[2];
+    softmax_grad(1, sB, dpB, lB, dB, pB, gB);
+    bf16x8 trB[2 * DB][2];
+    read_tr(1, trB);
+#pragma unroll
+    for (int i = 0; i < PM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase 4: dV, dK += sub-block B.
+    grad_mfma(trB, pB, gB);
     dma_wait();
     __syncthreads();
   };
