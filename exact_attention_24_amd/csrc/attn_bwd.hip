@@ -438,24 +438,20 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   // diagonal and any keys at or past L. In every earlier tile all keys are
   // below L and, with a causal mask, below m0, so all are visible. Lanes whose
   // query is at or past L compute on zero rows and are discarded at the store.
+  //
+  // One tile is two 32-key blocks 0 and 1, laid out in phases separated by
+  // scheduling fences (as in the dK/dV kernel): the exp/VALU work of one block
+  // runs under the MFMAs of the other and LDS reads run a phase ahead. The
+  // next tile's loads are issued first (past the end they read zeros and touch
+  // no memory), so the tile body is a single basic block.
   auto step = [&](int j, const int st, const bool MASKED) {
     const int n0 = j * BN;
-    if (j + 1 < nt) {
-      kdma.load(lds_base(st ? k0_ : k1_), n0 + BN);
-      vdma.load(lds_base(st ? v0_ : v1_), n0 + BN);
-    }
+    kdma.load(lds_base(st ? k0_ : k1_), n0 + BN);
+    vdma.load(lds_base(st ? v0_ : v1_), n0 + BN);
     const lds_t* Kt = lds_base(st ? k1_ : k0_);
     const lds_t* Vt = lds_base(st ? v1_ : v0_);
-    // One 32-key block at a time keeps only one S^T and one dP^T block live.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = mfma32x32x16_z(ad.rowop(Kt, kb * 32, 0), qreg[0]);
-      f32x16 dp = mfma32x32x16_z(ad.rowop(Vt, kb * 32, 0), doreg[0]);
-#pragma unroll
-      for (int ds = 1; ds < DS; ++ds) {
-        s = mfma32x32x16(ad.rowop(Kt, kb * 32, ds), qreg[ds], s);
-        dp = mfma32x32x16(ad.rowop(Vt, kb * 32, ds), doreg[ds], dp);
-      }
+
+    auto softmax_grad = [&](int kb, const f32x16& s, f32x16& dp, bf16x8* gb) {
       // Element i is key n0 + kb*32 + hi*4 + c (c = (i/4)*8 + i%4) against this
       // lane's query; it is visible iff c <= lim.
       const int lim = (CAUSAL ? min(q, L - 1) : L - 1) - n0 - kb * 32 - hi * 4;
@@ -465,14 +461,75 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
         if (MASKED) p = ((i >> 2) * 8 + (i & 3)) <= lim ? p : 0.f;
         dp[i] = p * (dp[i] - dq_delta);
       }
+      gb[0] = pack8(dp, 0);
+      gb[1] = pack8(dp, 1);
+    };
+    auto read_tr = [&](int kb, bf16x8* kt) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16x8 dsb = pack8(dp, h);
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          acc[db] = mfma32x32x16(ad.trop(Kt, kb * 32 + h * 16, db), dsb, acc[db]);
+        for (int db = 0; db < DB; ++db) kt[h * DB + db] = ad.trop(Kt, kb * 32 + h * 16, db);
+    };
+    auto dq_mfma = [&](const bf16x8* kt, const bf16x8* gb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16(kt[h * DB + db], gb[h], acc[db]);
+    };
+
+    // Operands are read just ahead of their MFMAs (two waves per SIMD cover
+    // the LDS latency; a deeper lookahead would not fit in 256 VGPRs).
+    constexpr int PM = 2 * DS;  // score MFMAs per key block
+    auto scores = [&](int kb, f32x16& s, f32x16& dp) {
+      s = mfma32x32x16_z(ad.rowop(Kt, kb * 32, 0), qreg[0]);
+      dp = mfma32x32x16_z(ad.rowop(Vt, kb * 32, 0), doreg[0]);
+#pragma unroll
+      for (int ds = 1; ds < DS; ++ds) {
+        s = mfma32x32x16(ad.rowop(Kt, kb * 32, ds), qreg[ds], s);
+        dp = mfma32x32x16(ad.rowop(Vt, kb * 32, ds), doreg[ds], dp);
       }
+    };
+    // Phase 1: S^T, dP^T of block 0.
+    f32x16 s0, dp0;
+    scores(0, s0, dp0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < PM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < PM - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase 2: S^T, dP^T of block 1; VALU of block 0.
+    f32x16 s1, dp1;
+    scores(1, s1, dp1);
+    bf16x8 g0[2];
+    softmax_grad(0, s0, dp0, g0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < PM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 5, 0);
+      if (i < PM - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase 3: dQ^T += K^T dS^T of block 0; VALU of block 1.
+    bf16x8 kt0[2 * DB];
+    read_tr(0, kt0);
+    dq_mfma(kt0, g0);
+    bf16x8 g1[2];
+    softmax_grad(1, s1, dp1, g1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 10, 0);
+      if (i < 2 * DB - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase 4: dQ^T += K^T dS^T of block 1.
+    bf16x8 kt1[2 * DB];
+    read_tr(1, kt1);
+    dq_mfma(kt1, g1);
     dma_wait();
     __syncthreads();
   };
