@@ -32,7 +32,8 @@ class Workload:
 
     ``seqlen_range`` (inclusive) switches on a padded variable-length batch:
     one length per sequence, drawn uniformly from the range after the tensors.
-    ``with_grad`` also draws the upstream gradient dO.
+    ``with_grad`` also draws the upstream gradient dO. ``H_kv`` (default H)
+    gives K and V fewer heads than Q (grouped- or multi-query attention).
     """
 
     name: str
@@ -46,6 +47,11 @@ class Workload:
     seqlen_range: Optional[tuple[int, int]] = None
     with_grad: bool = False
     description: str = ""
+    H_kv: Optional[int] = None
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.H_kv is None else self.H_kv
 
     @property
     def scale(self) -> float:
@@ -73,6 +79,10 @@ WORKLOADS = {
         Workload("causal_fwdbwd_bf16_b2_h16_n8192_d128", 2, 16, 8192, 128, "bf16", True, 1005,
                  with_grad=True,
                  description="forward + recompute backward, causal, bf16, B=2 H=16 N=8192 d=128"),
+        Workload("gqa_causal_bf16_b2_h32_hkv8_n4096_d128", 2, 32, 4096, 128, "bf16", True, 1006,
+                 with_grad=True, H_kv=8,
+                 description="grouped-query attention, 32 query heads over 8 K/V heads (the "
+                             "8:1 grouping of the pages' example), causal, bf16, fwd+bwd"),
     ]
 }
 
@@ -89,29 +99,30 @@ def draw_seqlens(gen: torch.Generator, B: int, lo: int, hi: int) -> torch.Tensor
 def make_inputs(B: int, H: int, N: int, d: int, dtype: torch.dtype = torch.bfloat16,
                 seed: int = 0, with_grad: bool = False,
                 seqlen_range: Optional[tuple[int, int]] = None,
-                std: float = 1.0) -> dict:
+                std: float = 1.0, H_kv: Optional[int] = None) -> dict:
     """Draw Q, K, V (and dO, then seqlens) on the CPU from one seeded generator.
 
     The draw order is fixed (Q, K, V, dO, seqlens) so a workload is the same
-    bits on every machine. Returns CPU tensors in ``dtype``; ``seqlens`` is an
-    int32 [B] tensor or None.
+    bits on every machine. K and V have H_kv heads (default H). Returns CPU
+    tensors in ``dtype``; ``seqlens`` is an int32 [B] tensor or None.
     """
     gen = torch.Generator(device="cpu")
     gen.manual_seed(int(seed))
-    shape = (B, H, N, d)
+    kv_heads = H if H_kv is None else H_kv
 
-    def draw() -> torch.Tensor:
-        x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    def draw(heads: int) -> torch.Tensor:
+        x = torch.randn((B, heads, N, d), generator=gen, dtype=torch.float32)
         if std != 1.0:
             x = x * std
         return x.to(dtype).contiguous()
 
-    out = {"q": draw(), "k": draw(), "v": draw()}
-    out["do"] = draw() if with_grad else None
+    out = {"q": draw(H), "k": draw(kv_heads), "v": draw(kv_heads)}
+    out["do"] = draw(H) if with_grad else None
     out["seqlens"] = (draw_seqlens(gen, B, *seqlen_range)
                       if seqlen_range is not None else None)
     return out
 
 
 def make_workload_inputs(w: Workload) -> dict:
-    return make_inputs(w.B, w.H, w.N, w.d, w.torch_dtype, w.seed, w.with_grad, w.seqlen_range)
+    return make_inputs(w.B, w.H, w.N, w.d, w.torch_dtype, w.seed, w.with_grad, w.seqlen_range,
+                       H_kv=w.H_kv)

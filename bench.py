@@ -138,6 +138,69 @@ def bench_backward(torch, ea, steps, warmup=3):
             "flop_convention": "10*B*H*N^2*d/2 (5 GEMMs, causal half); executed = 14*B*H*N^2*d/2"}
 
 
+SUITE_WORKLOADS = ["mha_bf16_b4_h16_n2048_d64", "causal_bf16_b2_h32_n4096_d128",
+                   "varlen_bf16_b8_h16_n2048_d128", "causal_fwdbwd_bf16_b2_h16_n8192_d128",
+                   "gqa_causal_bf16_b2_h32_hkv8_n4096_d128"]
+SWEEP_N = [2048, 4096, 8192, 16384]
+FLUSH_BYTES = 512 << 20  # larger than the 256 MiB Infinity Cache
+
+
+def time_launches(torch, fn, stream, warmup, steps):
+    """Per-launch HIP-event times (ms), sorted, after `warmup` untimed launches."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)
+
+
+def bench_suite(torch, ea, steps, warmup):
+    """Forward timings of every workload and of a context sweep (B=2 H=32 d=128
+    causal, N = 2K..16K). A 512 MiB buffer is written before each case so no
+    case starts with its inputs in the Infinity Cache. One JSON line per case:
+    median and P90 launch times and TFLOPS at the median."""
+    from attn_inputs import WORKLOADS, make_workload_inputs, Workload
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    cases = [(WORKLOADS[n], None) for n in SUITE_WORKLOADS]
+    cases += [(Workload(f"sweep_causal_bf16_b2_h32_n{n}_d128", 2, 32, n, 128, "bf16", True, 2000 + n), n)
+              for n in SWEEP_N]
+    for w, sweep_n in cases:
+        if sweep_n is None:
+            x = make_workload_inputs(w)
+            q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+            seqlens = x["seqlens"].to(dev) if x.get("seqlens") is not None else None
+            lens = x["seqlens"].tolist() if seqlens is not None else [w.N] * w.B
+        else:  # timing only: seeded normal inputs drawn on the device
+            g = torch.Generator(device=dev)
+            g.manual_seed(w.seed)
+            q, k, v = (torch.randn((w.B, w.H, w.N, w.d), generator=g, device=dev).to(torch.bfloat16)
+                       for _ in range(3))
+            seqlens, lens = None, [w.N] * w.B
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        flops = sum(fwd_flops(1, w.H, L, w.d, w.causal) for L in lens)
+        flush.fill_(1)
+        per = time_launches(torch, lambda: ea.attn_fwd(q, k, v, scale=w.scale, causal=w.causal,
+                                                       seqlens=seqlens, out=o, lse=lse),
+                            stream, warmup, steps)
+        med, p90 = per[len(per) // 2], per[int(0.9 * (len(per) - 1))]
+        print(json.dumps({"mode": "suite", "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                          "causal": w.causal, "varlen": seqlens is not None,
+                          "gflop": round(flops / 1e9, 2), "ms_median": round(med, 4),
+                          "ms_p90": round(p90, 4), "tflops_median": round(flops / (med * 1e-3) / 1e12, 1),
+                          "pct_of_bf16_peak": round(100 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)}),
+              flush=True)
+        del q, k, v, o, lse
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,9 +211,11 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=10,
                     help="timed backward passes on the causal B=2 H=16 N=8192 d=128 workload "
                          "(reported under \"bwd\"; 0 skips them)")
-    ap.add_argument("--mode", choices=["fwd", "bwd", "copy"], default="fwd",
-                    help="fwd: the benchmark; copy: a plain device copy of known size, whose "
-                         "FETCH_SIZE/WRITE_SIZE counters calibrate the traffic figure")
+    ap.add_argument("--mode", choices=["fwd", "bwd", "copy", "suite"], default="fwd",
+                    help="fwd: the benchmark; bwd: the backward alone; suite: forward timings "
+                         "of every workload plus a context sweep (one JSON line each); copy: a "
+                         "plain device copy of known size, whose FETCH_SIZE/WRITE_SIZE counters "
+                         "calibrate the traffic figure")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -164,6 +229,9 @@ def main():
     import exact_attention_24_amd as ea
     if args.mode == "bwd":
         print(json.dumps({"mode": "bwd", **bench_backward(torch, ea, args.steps, args.warmup)}), flush=True)
+        return
+    if args.mode == "suite":
+        bench_suite(torch, ea, args.steps, args.warmup)
         return
     from attn_inputs import WORKLOADS, make_workload_inputs
 

@@ -24,8 +24,8 @@ ATTN_OK = 0
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 # Every function include/attn.h declares.
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string",
-                    "attn_last_error")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_gqa", "attn_bwd", "attn_bwd_gqa",
+                    "attn_bwd_workspace_bytes", "attn_status_string", "attn_last_error")
 
 _lib = None
 
@@ -49,11 +49,16 @@ def lib() -> ctypes.CDLL:
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     L.attn_fwd.restype = i32
+    L.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
+    L.attn_fwd_gqa.restype = i32
     L.attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                            i32, i32, i32, i32, i32, f32, i32, vp, vp]
     L.attn_bwd.restype = i32
+    L.attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                               i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
+    L.attn_bwd_gqa.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -116,18 +121,32 @@ def _seqlens_ptr(seqlens, B, device) -> int:
     return seqlens.data_ptr()
 
 
+def _kv_heads(q, k) -> int:
+    """K/V head count: k is [B, H_kv, N, d] with H_kv dividing q's H."""
+    if k is None or k.dim() != 4:
+        raise ValueError("k must be a 4-d [B, H_kv, N, d] tensor")
+    H, H_kv = q.shape[1], k.shape[1]
+    if H_kv < 1 or H % H_kv != 0:
+        raise ValueError(f"K/V head count {H_kv} must divide the query head count {H}")
+    return H_kv
+
+
 def attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
              seqlens=None, out=None, lse=None, return_lse: bool = True):
     """O = softmax(scale * Q K^T) V over [B, H, N, d] device tensors.
 
-    Returns (O, LSE) with LSE fp32 [B, H, N] (natural log), or O alone when
-    ``return_lse`` is False and no ``lse`` buffer is given.
+    k and v may have fewer heads than q ([B, H_kv, N, d], H_kv dividing H):
+    query head h then reads K/V head h // (H // H_kv) (grouped- or
+    multi-query attention). Returns (O, LSE) with LSE fp32 [B, H, N] (natural
+    log), or O alone when ``return_lse`` is False and no ``lse`` buffer is given.
     """
     import torch
     B, H, N, d = q.shape
     dev = q.device
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(name, t, (B, H, N, d), q.dtype, dev)
+    H_kv = _kv_heads(q, k)
+    _check_tensor("q", q, (B, H, N, d), q.dtype, dev)
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, (B, H_kv, N, d), q.dtype, dev)
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -138,11 +157,17 @@ def attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     if lse is not None:
         _check_tensor("lse", lse, (B, H, N), torch.float32, dev)
-    st = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                        lse.data_ptr() if lse is not None else 0, B, H, N, d, code,
-                        float(scale), int(bool(causal)), _seqlens_ptr(seqlens, B, dev),
-                        _stream_handle(dev))
-    _check(st, "attn_fwd")
+    lse_ptr = lse.data_ptr() if lse is not None else 0
+    if H_kv == H:
+        st = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                            B, H, N, d, code, float(scale), int(bool(causal)),
+                            _seqlens_ptr(seqlens, B, dev), _stream_handle(dev))
+        _check(st, "attn_fwd")
+    else:
+        st = lib().attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                                B, H, H_kv, N, d, code, float(scale), int(bool(causal)),
+                                _seqlens_ptr(seqlens, B, dev), _stream_handle(dev))
+        _check(st, "attn_fwd_gqa")
     return (out, lse) if lse is not None else out
 
 
@@ -152,12 +177,16 @@ def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int, dtype_code: int = D
 
 def attn_bwd(q, k, v, o, do, lse, *, scale: Optional[float] = None, causal: bool = False,
              seqlens=None, dq=None, dk=None, dv=None, workspace=None):
-    """Recompute-based backward. Returns (dQ, dK, dV) in the input dtype."""
+    """Recompute-based backward. Returns (dQ, dK, dV) in the input dtype; with
+    grouped K/V heads dK, dV have k's shape and sum over each group."""
     import torch
     B, H, N, d = q.shape
     dev = q.device
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+    H_kv = _kv_heads(q, k)
+    for name, t in (("q", q), ("o", o), ("do", do)):
         _check_tensor(name, t, (B, H, N, d), q.dtype, dev)
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, (B, H_kv, N, d), q.dtype, dev)
     _check_tensor("lse", lse, (B, H, N), torch.float32, dev)
     code = _dtype_code(q)
     if scale is None:
@@ -165,17 +194,22 @@ def attn_bwd(q, k, v, o, do, lse, *, scale: Optional[float] = None, causal: bool
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_tensor(name, t, (B, H, N, d), q.dtype, dev)
+    _check_tensor("dq", dq, (B, H, N, d), q.dtype, dev)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, (B, H_kv, N, d), q.dtype, dev)
     need = attn_bwd_workspace_bytes(B, H, N, d, code)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device buffer")
     nbytes = workspace.numel() * workspace.element_size()
-    st = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                        workspace.data_ptr(), nbytes, B, H, N, d, code, float(scale),
-                        int(bool(causal)), _seqlens_ptr(seqlens, B, dev), _stream_handle(dev))
-    _check(st, "attn_bwd")
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), nbytes)
+    tail = (code, float(scale), int(bool(causal)), _seqlens_ptr(seqlens, B, dev), _stream_handle(dev))
+    if H_kv == H:
+        st = lib().attn_bwd(*ptrs, B, H, N, d, *tail)
+        _check(st, "attn_bwd")
+    else:
+        st = lib().attn_bwd_gqa(*ptrs, B, H, H_kv, N, d, *tail)
+        _check(st, "attn_bwd_gqa")
     return dq, dk, dv

@@ -35,6 +35,13 @@ attn_status check_sizes(int B, int H, int N, int d, attn_dtype dtype) {
 
 bool scale_ok(float scale) { return isfinite(scale) && scale > 0.f; }
 
+// Grouped K/V heads: H_kv must divide H (H_kv = H is plain multi-head
+// attention, H_kv = 1 multi-query attention).
+attn_status check_heads(int H, int H_kv) {
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
 size_t attn_bwd_section_bytes(int B, int H, int N) {
   const size_t rows = (size_t)B * H * N;
   return ((rows * sizeof(float) + 255) / 256) * 256;
@@ -56,11 +63,12 @@ const char* attn_status_string(attn_status s) {
 
 const char* attn_last_error(void) { return g_last_error; }
 
-attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                     int N, int d, attn_dtype dtype, float scale, int causal,
-                     const int32_t* seqlens, attn_stream_t stream) {
+attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H, int H_kv, int N, int d, attn_dtype dtype, float scale, int causal,
+                         const int32_t* seqlens, attn_stream_t stream) {
   attn_status st = check_sizes(B, H, N, d, dtype);
   if (st != ATTN_OK) return st;
+  if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
   if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
     return ATTN_ERR_INVALID_ARG;
@@ -69,7 +77,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 
   attn::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.seqlens = seqlens;
-  a.B = B; a.H = H; a.N = N;
+  a.B = B; a.H = H; a.N = N; a.H_kv = H_kv;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipStream_t s = (hipStream_t)stream;
@@ -82,18 +90,26 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   return ATTN_OK;
 }
 
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                     int N, int d, attn_dtype dtype, float scale, int causal,
+                     const int32_t* seqlens, attn_stream_t stream) {
+  return attn_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, dtype, scale, causal, seqlens, stream);
+}
+
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype dtype) {
   if (check_sizes(B, H, N, d, dtype) != ATTN_OK) return 0;
   // delta and log2-scaled LSE, one fp32 per row each, each section 256-byte aligned
   return 2 * attn_bwd_section_bytes(B, H, N);
 }
 
-attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                     const float* lse, void* dq, void* dk, void* dv, void* workspace,
-                     size_t workspace_bytes, int B, int H, int N, int d, attn_dtype dtype,
-                     float scale, int causal, const int32_t* seqlens, attn_stream_t stream) {
+attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                         const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, int B, int H, int H_kv, int N,
+                         int d, attn_dtype dtype, float scale, int causal, const int32_t* seqlens,
+                         attn_stream_t stream) {
   attn_status st = check_sizes(B, H, N, d, dtype);
   if (st != ATTN_OK) return st;
+  if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !workspace)
     return ATTN_ERR_INVALID_ARG;
   const void* t16[] = {q, k, v, o, dO, dq, dk, dv};
@@ -111,7 +127,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   a.delta = (float*)workspace;
   a.lse2 = (float*)((char*)workspace + attn_bwd_section_bytes(B, H, N));
   a.seqlens = seqlens;
-  a.B = B; a.H = H; a.N = N;
+  a.B = B; a.H = H; a.N = N; a.H_kv = H_kv;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = attn::launch_bwd_bf16(a, d, causal != 0, (hipStream_t)stream);
@@ -120,6 +136,14 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
     return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, int B, int H, int N, int d, attn_dtype dtype,
+                     float scale, int causal, const int32_t* seqlens, attn_stream_t stream) {
+  return attn_bwd_gqa(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d,
+                      dtype, scale, causal, seqlens, stream);
 }
 
 }  // extern "C"

@@ -147,15 +147,20 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int N = a.N;
   const int nkt = (N + BN - 1) / BN;
-  int bh, kt;
-  tile_order(blockIdx.x, nkt, a.B * a.H, false, bh, kt);
-  const int L = seq_len(a, bh / a.H);
+  // One workgroup per (batch, K/V head, key tile); with grouped K/V heads its
+  // dK, dV sum the contributions of the G = H / H_kv query heads that read
+  // this K/V head (query head h reads K/V head h / G).
+  int bkv, kt;
+  tile_order(blockIdx.x, nkt, a.B * a.H_kv, false, bkv, kt);
+  const int b = bkv / a.H_kv, G = a.H / a.H_kv;
+  const int hq0 = b * a.H + (bkv % a.H_kv) * G;  // first query head of the group
+  const int L = seq_len(a, b);
   const int n0 = kt * BN;
-  const size_t hoff = (size_t)bh * N * D;
-  const bf16_t* __restrict__ Kh = (const bf16_t*)a.k + hoff;
-  const bf16_t* __restrict__ Vh = (const bf16_t*)a.v + hoff;
-  bf16_t* __restrict__ dKh = (bf16_t*)a.dk + hoff;
-  bf16_t* __restrict__ dVh = (bf16_t*)a.dv + hoff;
+  const size_t kvoff = (size_t)bkv * N * D;
+  const bf16_t* __restrict__ Kh = (const bf16_t*)a.k + kvoff;
+  const bf16_t* __restrict__ Vh = (const bf16_t*)a.v + kvoff;
+  bf16_t* __restrict__ dKh = (bf16_t*)a.dk + kvoff;
+  bf16_t* __restrict__ dVh = (bf16_t*)a.dv + kvoff;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
   if (n0 >= L) {  // every key of this tile is padding: zero gradients
@@ -176,10 +181,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   const int nqt = ((L - q_begin + BM - 1) / BM + 1) & ~1;
   const float c2 = a.scale_log2;
 
-  const TileDma<D, BM, 4> qdma((const bf16_t*)a.q + hoff, L, wave, lane);
-  const TileDma<D, BM, 4> odma((const bf16_t*)a.dO + hoff, L, wave, lane);
-  const float* lse2_h = a.lse2 + (size_t)bh * N;
-  const float* delta_h = a.delta + (size_t)bh * N;
+  // Per query head of the group (set in the head loop below).
+  TileDma<D, BM, 4> qdma((const bf16_t*)a.q, L, wave, lane);
+  TileDma<D, BM, 4> odma((const bf16_t*)a.dO, L, wave, lane);
+  const float* lse2_h = a.lse2;
+  const float* delta_h = a.delta;
   // Stage st: Q tile, dO tile, then lse2[BM] and delta[BM] of the same rows.
   // Waves 0 and 2 both fetch lse2 and waves 1 and 3 both fetch delta (the
   // same bytes to the same place), which keeps the code free of branches.
@@ -189,7 +195,6 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     const int odd = wave & 1;
     vec64_dma(lds_base(st ? st1_ : st0_) + odd * (BM * 4), odd ? delta_h : lse2_h, L, q0, lane);
   };
-  load_tile(q_begin, 0);
 
   bf16x8 kreg[DS], vreg[DS];
 #pragma unroll
@@ -345,17 +350,27 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     __syncthreads();
   };
 
-  dma_wait();
-  __syncthreads();
-  int t = 0;
-  if (CAUSAL) {  // query tiles [n0, n0 + 128): the diagonal
-    step(0, 0, true);
-    step(1, 1, true);
-    t = 2;
-  }
-  for (; t < nqt; t += 2) {
-    step(t, 0, false);
-    step(t + 1, 1, false);
+  for (int g = 0; g < G; ++g) {
+    const size_t qoff = (size_t)(hq0 + g) * N;
+    qdma.head = (const bf16_t*)a.q + qoff * D;
+    odma.head = (const bf16_t*)a.dO + qoff * D;
+    lse2_h = a.lse2 + qoff;
+    delta_h = a.delta + qoff;
+    // Stage 0 is free: every wave passed the barrier that ended the previous
+    // head's last tile.
+    load_tile(q_begin, 0);
+    dma_wait();
+    __syncthreads();
+    int t = 0;
+    if (CAUSAL) {  // query tiles [n0, n0 + 128): the diagonal
+      step(0, 0, true);
+      step(1, 1, true);
+      t = 2;
+    }
+    for (; t < nqt; t += 2) {
+      step(t, 0, false);
+      step(t + 1, 1, false);
+    }
   }
 
   if (key < N) {
@@ -391,6 +406,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   const int L = seq_len(a, bh / a.H);
   const int m0 = mt * BM;
   const size_t hoff = (size_t)bh * N * D;
+  const size_t kvoff = (size_t)((bh / a.H) * a.H_kv + (bh % a.H) / (a.H / a.H_kv)) * N * D;
   const bf16_t* __restrict__ Qh = (const bf16_t*)a.q + hoff;
   const bf16_t* __restrict__ dOh = (const bf16_t*)a.dO + hoff;
   bf16_t* __restrict__ dQh = (bf16_t*)a.dq + hoff;
@@ -412,8 +428,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   const int nt = ((kv_end + BN - 1) / BN + 1) & ~1;
   const float c2 = a.scale_log2;
 
-  const TileDma<D, BN, 4> kdma((const bf16_t*)a.k + hoff, L, wave, lane);
-  const TileDma<D, BN, 4> vdma((const bf16_t*)a.v + hoff, L, wave, lane);
+  const TileDma<D, BN, 4> kdma((const bf16_t*)a.k + kvoff, L, wave, lane);
+  const TileDma<D, BN, 4> vdma((const bf16_t*)a.v + kvoff, L, wave, lane);
   kdma.load(lds_base(k0_), 0);
   vdma.load(lds_base(v0_), 0);
 
@@ -567,7 +583,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int heads = a.B * a.H;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(heads * ((a.N + 127) / 128))),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>),
+                     dim3((unsigned)(a.B * a.H_kv * ((a.N + 127) / 128))),
                      dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

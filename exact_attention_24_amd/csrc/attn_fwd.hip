@@ -79,6 +79,8 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   if (a.seqlens) L = min(max(a.seqlens[b], 0), N);
   const int m0 = mt * BM;
   const size_t hoff = (size_t)bh * N * D;
+  // Grouped K/V heads: query head h reads K/V head h / (H / H_kv).
+  const size_t kvoff = (size_t)(b * a.H_kv + (bh % a.H) / (a.H / a.H_kv)) * N * D;
   const bf16_t* __restrict__ Qh = (const bf16_t*)a.q + hoff;
   bf16_t* __restrict__ Oh = (bf16_t*)a.o + hoff;
   float* __restrict__ lse_h = a.lse ? a.lse + (size_t)bh * N : nullptr;
@@ -100,8 +102,8 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   const int w_end = (qw >= L) ? 0 : (CAUSAL ? min(L, qw + 32) : L);
   const int wnt = (w_end + BN - 1) / BN;                 // tiles this wave computes
 
-  const TileDma<D, BN, 4> kdma((const bf16_t*)a.k + hoff, N, wave, lane);
-  const TileDma<D, BN, 4> vdma((const bf16_t*)a.v + hoff, N, wave, lane);
+  const TileDma<D, BN, 4> kdma((const bf16_t*)a.k + kvoff, N, wave, lane);
+  const TileDma<D, BN, 4> vdma((const bf16_t*)a.v + kvoff, N, wave, lane);
   kdma.load(kst[0], 0);
   vdma.load(vst[0], 0);
 
@@ -256,9 +258,10 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a) {
   if (a.seqlens) L = min(max(a.seqlens[b], 0), N);
   const int m0 = mt * BM, q = m0 + lane;
   const size_t hoff = (size_t)bh * N * D;
+  const size_t kvoff = (size_t)(b * a.H_kv + (bh % a.H) / (a.H / a.H_kv)) * N * D;
   const float4* Qh = (const float4*)((const float*)a.q + hoff);
-  const float4* Kh = (const float4*)((const float*)a.k + hoff);
-  const float4* Vh = (const float4*)((const float*)a.v + hoff);
+  const float4* Kh = (const float4*)((const float*)a.k + kvoff);
+  const float4* Vh = (const float4*)((const float*)a.v + kvoff);
   float4* Oh = (float4*)((float*)a.o + hoff);
   const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
 

@@ -16,6 +16,7 @@ struct FwdArgs {
   float* lse;               // may be null
   const int32_t* seqlens;   // may be null
   int B, H, N;
+  int H_kv;                 // K/V heads; query head h reads K/V head h / (H / H_kv)
   float scale;              // softmax scale applied to q.k
   float scale_log2;         // scale * log2(e)
 };
@@ -34,6 +35,7 @@ struct BwdArgs {
   float* lse2;              // workspace: LSE * log2(e), fp32 [B,H,N] (0 on padded rows)
   const int32_t* seqlens;
   int B, H, N;
+  int H_kv;                 // K/V heads; query head h reads K/V head h / (H / H_kv)
   float scale;
   float scale_log2;
 };

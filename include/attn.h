@@ -23,6 +23,8 @@
  *    block skipping; the backward recomputes P from Q, K, V).
  *  - the AIInfra FlashAttention note on dpshk.com: §2.1 (finite initial row
  *    max), §2.3 (dV = P^T dO, dS = P o (dP - rowsum(dP o P)), dP = dO V^T).
+ *  - "Attention 算子优化..." §五 (grouped- and multi-query attention: several
+ *    query heads share one K/V head).
  *
  * Conventions shared by every entry point
  *  - Tensors are [B, H, N, d], contiguous, d fastest (element (b,h,i,c) sits at
@@ -92,6 +94,18 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      const int32_t* seqlens, attn_stream_t stream);
 
 /*
+ * attn_fwd_gqa - attn_fwd with grouped K/V heads ("Attention 算子优化..." §五).
+ *
+ * q, o are [B,H,N,d]; k, v are [B,H_kv,N,d]. Query head h attends with K/V
+ * head h / (H / H_kv): H_kv = H is attn_fwd, H_kv = 1 is multi-query
+ * attention. H_kv must divide H (ATTN_ERR_INVALID_ARG otherwise). All other
+ * arguments and outputs as for attn_fwd.
+ */
+attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int H_kv, int N, int d, attn_dtype dtype, float scale,
+                         int causal, const int32_t* seqlens, attn_stream_t stream);
+
+/*
  * attn_bwd_workspace_bytes - device workspace that attn_bwd needs for these sizes
  * (it holds D_i = rowsum(dO_i o O_i) and LSE_i * log2(e), fp32 [B,H,N] each).
  * Returns 0 for invalid sizes.
@@ -119,6 +133,20 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, int B, int H, int N, int d, attn_dtype dtype,
                      float scale, int causal, const int32_t* seqlens, attn_stream_t stream);
+
+/*
+ * attn_bwd_gqa - attn_bwd with grouped K/V heads (see attn_fwd_gqa).
+ *
+ * q, o, dO, dq are [B,H,N,d]; k, v, dk, dv are [B,H_kv,N,d]. dK and dV of a
+ * K/V head are the sums of the contributions of the H / H_kv query heads that
+ * read it, accumulated in a fixed order (deterministic). The workspace is
+ * attn_bwd_workspace_bytes(B, H, N, d, dtype) with the query head count H.
+ */
+attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                         const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, int B, int H, int H_kv, int N,
+                         int d, attn_dtype dtype, float scale, int causal,
+                         const int32_t* seqlens, attn_stream_t stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* attn_status_string(attn_status s);

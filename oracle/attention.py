@@ -39,6 +39,13 @@ Readings taken where the pages are silent (each is listed in the design notes):
     has no softmax; its output row is 0 and its LSE is -inf.
   * Queries and keys of one sequence share one valid length; causal alignment
     is top-left (query i sees keys 0..i).
+  * Grouped K/V heads ([OpOpt] §五: query heads fall into groups and each group
+    shares one K/V head; H_kv = 1 is multi-query attention): with k, v of shape
+    [B, H_kv, N, d], query head h uses K/V head h // (H // H_kv), i.e. groups
+    are runs of consecutive query heads (the pages do not fix the order; this
+    is the plain reading). In the backward a K/V head's gradient is the sum of
+    the per-query-head gradients of its group (the chain rule through the
+    shared tensor).
   * Backward ([AIInfra] §2.3 gives dV = P^T dO and dS = P o (dP - rowsum(dP o P))
     with dP = dO V^T; the scale factor on dQ and dK is not on the pages and
     follows from S = scale * Q K^T by the chain rule):
@@ -49,7 +56,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["scores", "mask", "softmax_three_pass", "attn_ref_head", "attn_ref_fwd",
+__all__ = ["scores", "mask", "softmax_three_pass", "attn_ref_head", "kv_head", "attn_ref_fwd",
            "attn_ref_rows", "attn_ref_bwd_head", "attn_ref_bwd"]
 
 
@@ -145,19 +152,30 @@ def attn_ref_head(q, k, v, scale: float, causal: bool = False, valid_len=None,
     return o, lse
 
 
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """K/V head read by query head h when H_kv K/V heads serve H query heads
+    ([OpOpt] §五): consecutive runs of H // H_kv query heads share one."""
+    if H_kv < 1 or H % H_kv:
+        raise ValueError(f"{H_kv} K/V heads cannot serve {H} query heads")
+    return h // (H // H_kv)
+
+
 def attn_ref_fwd(q, k, v, scale: float, causal: bool = False, seqlens=None):
-    """Forward over [B, H, N, d] inputs (any float type, upcast exactly to fp64).
+    """Forward over [B, H, N, d] queries and [B, H_kv, N, d] keys/values (any
+    float type, upcast exactly to fp64; H_kv = H is plain multi-head attention).
 
     Returns (O [B,H,N,d] fp64, LSE [B,H,N] fp64 natural log).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
     o = np.zeros((B, H, N, v.shape[-1]))
     lse = np.zeros((B, H, N))
     for b in range(B):
         L = _valid_len(seqlens, b, N)
         for h in range(H):
-            o[b, h], lse[b, h] = attn_ref_head(q[b, h], k[b, h], v[b, h], scale, causal, L)
+            g = kv_head(h, H, H_kv)
+            o[b, h], lse[b, h] = attn_ref_head(q[b, h], k[b, g], v[b, g], scale, causal, L)
     return o, lse
 
 
@@ -169,7 +187,8 @@ def attn_ref_rows(q, k, v, b: int, h: int, rows, scale: float, causal: bool = Fa
     """
     N = q.shape[2]
     L = _valid_len(seqlens, b, N)
-    return attn_ref_head(q[b, h], k[b, h], v[b, h], scale, causal, L, rows=rows)
+    g = kv_head(h, q.shape[1], k.shape[1])
+    return attn_ref_head(q[b, h], k[b, g], v[b, g], scale, causal, L, rows=rows)
 
 
 def attn_ref_bwd_head(q, k, v, do, scale: float, causal: bool = False, valid_len=None):
@@ -190,15 +209,21 @@ def attn_ref_bwd_head(q, k, v, do, scale: float, causal: bool = False, valid_len
 
 
 def attn_ref_bwd(q, k, v, do, scale: float, causal: bool = False, seqlens=None):
-    """Backward over [B, H, N, d] inputs. Returns (dQ, dK, dV) fp64."""
+    """Backward over [B, H, N, d] queries and [B, H_kv, N, d] keys/values.
+    Returns (dQ, dK, dV) fp64; dK and dV have the K/V shape, each K/V head
+    summing the gradients of the query heads that read it."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for b in range(B):
         L = _valid_len(seqlens, b, N)
         for h in range(H):
-            dq[b, h], dk[b, h], dv[b, h] = attn_ref_bwd_head(
-                q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, L)
+            g = kv_head(h, H, H_kv)
+            dq[b, h], dk_h, dv_h = attn_ref_bwd_head(
+                q[b, h], k[b, g], v[b, g], do[b, h], scale, causal, L)
+            dk[b, g] += dk_h
+            dv[b, g] += dv_h
     return dq, dk, dv

@@ -36,7 +36,9 @@ def golden(name: str) -> dict:
 def oracle_impl():
     import oracle.attention as A
     return types.SimpleNamespace(head=lambda *a, **kw: A.attn_ref_head(*a, **kw),
-                                 bwd_head=lambda *a, **kw: A.attn_ref_bwd_head(*a, **kw))
+                                 bwd_head=lambda *a, **kw: A.attn_ref_bwd_head(*a, **kw),
+                                 fwd=lambda *a, **kw: A.attn_ref_fwd(*a, **kw),
+                                 bwd=lambda *a, **kw: A.attn_ref_bwd(*a, **kw))
 
 
 def _rng(seed):
@@ -437,10 +439,82 @@ def pin_bwd_invariants(impl):
         _close(dv.sum(axis=0), do[:9].sum(axis=0), 1e-12, "sum dV (padded)")
 
 
+# ------------------------------------------------------ grouped K/V heads
+# These pins take the batch-level entry points: impl.fwd(q, k, v, scale, causal,
+# seqlens) -> (O, LSE) and impl.bwd(q, k, v, do, scale, causal, seqlens) ->
+# (dQ, dK, dV), with q [B,H,N,d] and k, v [B,H_kv,N,d].
+
+def pin_gqa_torch_sdpa(impl):
+    """Library special case: torch's fp64 CPU SDPA with enable_gqa, whose K/V
+    head for query head h is h // (H // H_kv) ([OpOpt] §五's grouping with
+    consecutive query heads per group), forward and autograd backward."""
+    for seed, (B, H, H_kv), causal in [(70, (2, 6, 2), False), (71, (1, 4, 1), True),
+                                       (72, (2, 8, 4), True)]:
+        r = _rng(seed)
+        n, d = 11, 5
+        q = r.standard_normal((B, H, n, d))
+        k, v = r.standard_normal((B, H_kv, n, d)), r.standard_normal((B, H_kv, n, d))
+        do = r.standard_normal((B, H, n, d))
+        o, _ = impl.fwd(q, k, v, 0.6, causal)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                               scale=0.6, enable_gqa=True)
+        _close(o, out.detach().numpy(), 1e-12, f"GQA O (H={H}, H_kv={H_kv})")
+        out.backward(torch.from_numpy(do))
+        dq, dk, dv = impl.bwd(q, k, v, do, 0.6, causal)
+        for a, t, nm in [(dq, tq, "dQ"), (dk, tk, "dK"), (dv, tv, "dV")]:
+            _close(a, t.grad.numpy(), 1e-12, f"GQA {nm} (H={H}, H_kv={H_kv})")
+
+
+def pin_gqa_finite_difference(impl):
+    """A shared K/V head's gradient is the derivative of L = sum(O o dO) through
+    every query head that reads it: central finite differences in fp64."""
+    r = _rng(73)
+    B, H, H_kv, n, d = 1, 3, 1, 5, 3
+    q = r.standard_normal((B, H, n, d))
+    k, v = r.standard_normal((B, H_kv, n, d)), r.standard_normal((B, H_kv, n, d))
+    do = r.standard_normal((B, H, n, d))
+    for causal in (False, True):
+        _, dk, dv = impl.bwd(q, k, v, do, 0.7, causal)
+        for which, g in ((1, dk), (2, dv)):
+            fd = np.zeros_like(g)
+            for idx in np.ndindex(g.shape):
+                args = [q, k.copy(), v.copy()]
+                args[which][idx] += 1e-6
+                lp = float(np.sum(impl.fwd(*args, 0.7, causal)[0] * do))
+                args[which][idx] -= 2e-6
+                lm = float(np.sum(impl.fwd(*args, 0.7, causal)[0] * do))
+                fd[idx] = (lp - lm) / 2e-6
+            err = np.max(np.abs(g - fd)) / max(np.max(np.abs(fd)), 1e-30)
+            assert err <= 1e-7, f"GQA {'dK' if which == 1 else 'dV'} finite-difference err {err:.2e}"
+
+
+def pin_gqa_padding(impl):
+    """Grouped heads with a padded batch: every query head of sequence b sees
+    only its first L_b keys; padded rows are 0 / -inf and get zero gradient."""
+    r = _rng(74)
+    B, H, H_kv, n, d = 2, 4, 2, 9, 3
+    q = r.standard_normal((B, H, n, d))
+    k, v = r.standard_normal((B, H_kv, n, d)), r.standard_normal((B, H_kv, n, d))
+    do = r.standard_normal((B, H, n, d))
+    sl = np.array([6, 9])
+    o, lse = impl.fwd(q, k, v, 0.5, False, sl)
+    for h in range(H):
+        g = h // (H // H_kv)
+        ref_o, ref_l = impl.head(q[0, h, :6], k[0, g, :6], v[0, g, :6], 0.5)
+        _close(o[0, h, :6], ref_o, 1e-13, "GQA padded O")
+        _close(lse[0, h, :6], ref_l, 1e-13, "GQA padded LSE")
+    assert np.all(o[0, :, 6:] == 0) and np.all(np.isneginf(lse[0, :, 6:]))
+    dq, dk, dv = impl.bwd(q, k, v, do, 0.5, False, sl)
+    assert np.all(dq[0, :, 6:] == 0) and np.all(dk[0, :, 6:] == 0) and np.all(dv[0, :, 6:] == 0)
+
+
+GQA_PINS = [pin_gqa_torch_sdpa, pin_gqa_finite_difference, pin_gqa_padding]
+
 FWD_PINS = [pin_two_block_example, pin_merge_example, pin_safe_softmax_example,
             pin_hand_case_noncausal, pin_hand_case_causal, pin_hand_case_scaled,
             pin_rows_sum_to_one, pin_shift_invariance, pin_value_shift, pin_permutation,
             pin_zero_query, pin_causal_first_row, pin_single_key, pin_padding,
             pin_identical_queries, pin_large_scores, pin_torch_sdpa, pin_online_merge]
 BWD_PINS = [pin_bwd_finite_difference, pin_bwd_torch_autograd, pin_bwd_invariants]
-ALL_PINS = FWD_PINS + BWD_PINS
+ALL_PINS = FWD_PINS + BWD_PINS + GQA_PINS

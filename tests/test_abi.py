@@ -99,6 +99,29 @@ def test_bwd_rejects_bad_arguments(L, kw, want):
     assert bwd(L, ws_bytes, **kw) == want
 
 
+def fwd_gqa(L, H=4, H_kv=2, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, N=64, d=64, dtype=1, scale=0.125, causal=0, seqlens=0)
+    a.update(kw)
+    return L.attn_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], H, H_kv, a["N"], a["d"],
+                          a["dtype"], a["scale"], a["causal"], a["seqlens"], 0)
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 0), (4, -1), (4, 3), (4, 8), (6, 4)])
+def test_gqa_rejects_bad_head_counts(L, H, H_kv):
+    assert fwd_gqa(L, H, H_kv, q=0) == INVALID  # still rejected (null q) ...
+    assert fwd_gqa(L, H, H_kv) == INVALID       # ... and for the head count alone
+
+
+def test_gqa_validates_like_fwd(L):
+    assert fwd_gqa(L, 4, 2, d=96) == UNSUPPORTED
+    assert fwd_gqa(L, 4, 2, scale=0.0) == INVALID
+    ws = L.attn_bwd_workspace_bytes(1, 4, 64, 64, 1)
+    assert L.attn_bwd_gqa(P, P, P, P, P, P, P, P, P, P, ws, 1, 4, 3, 64, 64, 1, 0.125, 0, 0,
+                          0) == INVALID
+    assert L.attn_bwd_gqa(P, P, P, P, P, P, P, P, P, 0, ws, 1, 4, 2, 64, 64, 1, 0.125, 0, 0,
+                          0) == INVALID
+
+
 def test_workspace_bytes(L):
     # two fp32 [B,H,N] sections (delta, log2-scaled LSE), each rounded up to 256 bytes
     assert L.attn_bwd_workspace_bytes(2, 16, 8192, 128, 1) == 2 * (2 * 16 * 8192 * 4)

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as A
-from tests.oracle_pins import ALL_PINS, BWD_PINS, FWD_PINS
+from tests.oracle_pins import ALL_PINS, BWD_PINS, FWD_PINS, GQA_PINS
 
 
 def _run_pins(impl, pins):
@@ -160,5 +160,38 @@ def test_backward_mutant_is_caught(name):
 
 def test_unmutated_backward_copy_passes():
     """The mutant factory with no mutation passes every pin (the harness is sound)."""
-    impl = types.SimpleNamespace(head=A.attn_ref_head, bwd_head=_bwd_factory("none"))
+    impl = types.SimpleNamespace(head=A.attn_ref_head, bwd_head=_bwd_factory("none"),
+                                 fwd=A.attn_ref_fwd, bwd=A.attn_ref_bwd)
     assert _run_pins(impl, ALL_PINS) == []
+
+
+# ---- grouped K/V head mutants
+
+def _kv_interleaved(h, H, H_kv):
+    return h % H_kv
+
+
+def _gqa_bwd_overwrite(q, k, v, do, scale, causal=False, seqlens=None):
+    """The batched backward with the group sum replaced by the last head's term."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    B, H, N, _ = q.shape
+    H_kv = k.shape[1]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        L = N if seqlens is None else int(seqlens[b])
+        for h in range(H):
+            g = h // (H // H_kv)
+            dq[b, h], dk[b, g], dv[b, g] = A.attn_ref_bwd_head(q[b, h], k[b, g], v[b, g], do[b, h],
+                                                               scale, causal, L)
+    return dq, dk, dv
+
+
+def test_gqa_interleaved_grouping_is_caught(monkeypatch):
+    monkeypatch.setattr(A, "kv_head", _kv_interleaved)
+    impl = types.SimpleNamespace(head=A.attn_ref_head, fwd=A.attn_ref_fwd, bwd=A.attn_ref_bwd)
+    assert _run_pins(impl, GQA_PINS), "interleaved K/V grouping passed every grouped-head pin"
+
+
+def test_gqa_missing_group_sum_is_caught():
+    impl = types.SimpleNamespace(head=A.attn_ref_head, fwd=A.attn_ref_fwd, bwd=_gqa_bwd_overwrite)
+    assert _run_pins(impl, GQA_PINS), "dropped group sum passed every grouped-head pin"
