@@ -41,7 +41,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     causal: bool
     seed: int
     seqlen_range: Optional[tuple[int, int]] = None
@@ -59,7 +59,7 @@ class Workload:
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[self.dtype]
 
 
 # The five workloads of this project: shapes, masks and precisions.
@@ -79,6 +79,9 @@ WORKLOADS = {
         Workload("causal_fwdbwd_bf16_b2_h16_n8192_d128", 2, 16, 8192, 128, "bf16", True, 1005,
                  with_grad=True,
                  description="forward + recompute backward, causal, bf16, B=2 H=16 N=8192 d=128"),
+        Workload("causal_f16_b2_h32_n4096_d128", 2, 32, 4096, 128, "f16", True, 1007,
+                 with_grad=True,
+                 description="the causal B=2 H=32 N=4096 d=128 shape with fp16 inputs, fwd+bwd"),
         Workload("gqa_causal_bf16_b2_h32_hkv8_n4096_d128", 2, 32, 4096, 128, "bf16", True, 1006,
                  with_grad=True, H_kv=8,
                  description="grouped-query attention, 32 query heads over 8 K/V heads (the "

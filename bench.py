@@ -140,7 +140,7 @@ def bench_backward(torch, ea, steps, warmup=3):
 
 SUITE_WORKLOADS = ["mha_bf16_b4_h16_n2048_d64", "causal_bf16_b2_h32_n4096_d128",
                    "varlen_bf16_b8_h16_n2048_d128", "causal_fwdbwd_bf16_b2_h16_n8192_d128",
-                   "gqa_causal_bf16_b2_h32_hkv8_n4096_d128"]
+                   "gqa_causal_bf16_b2_h32_hkv8_n4096_d128", "causal_f16_b2_h32_n4096_d128"]
 SWEEP_N = [2048, 4096, 8192, 16384]
 FLUSH_BYTES = 512 << 20  # larger than the 256 MiB Infinity Cache
 

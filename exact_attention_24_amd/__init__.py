@@ -16,13 +16,15 @@ import pathlib
 from typing import Optional
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string",
-           "AttnError", "lib", "LIB_PATH", "DTYPE_F32", "DTYPE_BF16", "EXPORTED_SYMBOLS"]
+           "AttnError", "lib", "LIB_PATH", "DTYPE_F32", "DTYPE_BF16", "DTYPE_F16",
+           "EXPORTED_SYMBOLS"]
 
 LIB_PATH = pathlib.Path(__file__).resolve().parent / "lib" / "libattn.so"
 
 ATTN_OK = 0
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_F16 = 2
 # Every function include/attn.h declares.
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_gqa", "attn_bwd", "attn_bwd_gqa",
                     "attn_bwd_workspace_bytes", "attn_status_string", "attn_last_error")
@@ -88,9 +90,11 @@ def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
         return DTYPE_BF16
+    if t.dtype == torch.float16:
+        return DTYPE_F16
     if t.dtype == torch.float32:
         return DTYPE_F32
-    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16, float16 or float32")
 
 
 def _stream_handle(device) -> int:

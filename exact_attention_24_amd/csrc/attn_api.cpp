@@ -23,7 +23,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 attn_status check_sizes(int B, int H, int N, int d, attn_dtype dtype) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
-  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16)
+    return ATTN_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   // Workgroup counts and per-head row offsets must fit the kernels' 32-bit
   // index arithmetic: (B*H) * ceil(N/64) workgroups and N*d elements per head.
@@ -81,8 +82,9 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = dtype == ATTN_DTYPE_BF16 ? attn::launch_fwd_bf16(a, d, causal != 0, s)
-                                          : attn::launch_fwd_f32(a, d, causal != 0, s);
+  hipError_t e = dtype == ATTN_DTYPE_F32
+                     ? attn::launch_fwd_f32(a, d, causal != 0, s)
+                     : attn::launch_fwd_16(a, d, causal != 0, dtype == ATTN_DTYPE_F16, s);
   if (e != hipSuccess) {
     record_hip_error(e, "attn_fwd launch");
     return ATTN_ERR_HIP;
@@ -119,7 +121,7 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
     return ATTN_ERR_INVALID_ARG;
   if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d, dtype)) return ATTN_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
-  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
 
   attn::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
@@ -130,7 +132,7 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
   a.B = B; a.H = H; a.N = N; a.H_kv = H_kv;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = attn::launch_bwd_bf16(a, d, causal != 0, (hipStream_t)stream);
+  hipError_t e = attn::launch_bwd_16(a, d, causal != 0, dtype == ATTN_DTYPE_F16, (hipStream_t)stream);
   if (e != hipSuccess) {
     record_hip_error(e, "attn_bwd launch");
     return ATTN_ERR_HIP;

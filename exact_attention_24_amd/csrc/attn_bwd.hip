@@ -43,15 +43,15 @@ __device__ __forceinline__ int seq_len(const BwdArgs& a, int b) {
 // result and values for d = db*32 + g*8 + hi*4 + {0..3}. A lane with
 // valid == false stores zeros (selected, so a non-finite accumulator in a
 // discarded lane cannot leak through a multiply by 0).
-template <int DB>
-__device__ __forceinline__ void store_rowT(bf16_t* rowp, const f32x16* acc, float mul, bool valid,
+template <int DB, bool F16>
+__device__ __forceinline__ void store_rowT(e16_t* rowp, const f32x16* acc, float mul, bool valid,
                                            int hi) {
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t w0 = pack_bf16x2(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul);
-      const uint32_t w1 = pack_bf16x2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
+      const uint32_t w0 = pack2<F16>(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul);
+      const uint32_t w1 = pack2<F16>(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
       const u32x2 w = {valid ? w0 : 0u, valid ? w1 : 0u};
       gstore8(rowp + db * 32 + g * 8 + hi * 4, w);
     }
@@ -78,13 +78,13 @@ struct TileAddr {
       tr[db][1] = tile_off_col<D>(r + 8, col);
     }
   }
-  __device__ __forceinline__ bf16x8 rowop(const lds_t* t, int row0, int ds) const {
-    return as_bf16x8(lds_load16(t + row[ds] + row0 * (D * 2)));
+  __device__ __forceinline__ e16x8 rowop(const lds_t* t, int row0, int ds) const {
+    return as_e16x8(lds_load16(t + row[ds] + row0 * (D * 2)));
   }
-  __device__ __forceinline__ bf16x8 trop(const lds_t* t, int row0, int db) const {
+  __device__ __forceinline__ e16x8 trop(const lds_t* t, int row0, int db) const {
     const u32x2 lo = lds_load_tr16(t + tr[db][0] + row0 * (D * 2));
     const u32x2 up = lds_load_tr16(t + tr[db][1] + row0 * (D * 2));
-    return join_bf16x8(lo, up);
+    return join_e16x8(lo, up);
   }
 };
 
@@ -92,7 +92,7 @@ struct TileAddr {
 // delta_i = sum_d dO_i[d] * O_i[d] in fp32 and lse2_i = LSE_i * log2(e);
 // both 0 for padded rows.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool F16>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a) {
   constexpr int TPR = D / 8, RPB = 256 / TPR;
   const int tid = threadIdx.x;
@@ -105,11 +105,11 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a) {
     const int bh = (int)(row / a.N), q = (int)(row % a.N);
     valid = q < seq_len(a, bh / a.H);
     if (valid) {
-      const u32x4 o = gload16((const bf16_t*)a.o + row * D + c * 8);
-      const u32x4 g = gload16((const bf16_t*)a.dO + row * D + c * 8);
+      const u32x4 o = gload16((const e16_t*)a.o + row * D + c * 8);
+      const u32x4 g = gload16((const e16_t*)a.dO + row * D + c * 8);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        part += bf16_lo(o[i]) * bf16_lo(g[i]) + bf16_hi(o[i]) * bf16_hi(g[i]);
+        part += unpack_lo<F16>(o[i]) * unpack_lo<F16>(g[i]) + unpack_hi<F16>(o[i]) * unpack_hi<F16>(g[i]);
     }
   }
 #pragma unroll
@@ -132,7 +132,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a) {
 //   dS             = P o (dP - delta)
 //   dK^T (d x key) += Q^T dS       A = Q^T (transposing LDS read),  B = dS
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   constexpr int BN = 128, BM = 64;
   constexpr int TILE = BM * D * 2;
@@ -157,10 +157,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   const int L = seq_len(a, b);
   const int n0 = kt * BN;
   const size_t kvoff = (size_t)bkv * N * D;
-  const bf16_t* __restrict__ Kh = (const bf16_t*)a.k + kvoff;
-  const bf16_t* __restrict__ Vh = (const bf16_t*)a.v + kvoff;
-  bf16_t* __restrict__ dKh = (bf16_t*)a.dk + kvoff;
-  bf16_t* __restrict__ dVh = (bf16_t*)a.dv + kvoff;
+  const e16_t* __restrict__ Kh = (const e16_t*)a.k + kvoff;
+  const e16_t* __restrict__ Vh = (const e16_t*)a.v + kvoff;
+  e16_t* __restrict__ dKh = (e16_t*)a.dk + kvoff;
+  e16_t* __restrict__ dVh = (e16_t*)a.dv + kvoff;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
   if (n0 >= L) {  // every key of this tile is padding: zero gradients
@@ -182,8 +182,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   const float c2 = a.scale_log2;
 
   // Per query head of the group (set in the head loop below).
-  TileDma<D, BM, 4> qdma((const bf16_t*)a.q, L, wave, lane);
-  TileDma<D, BM, 4> odma((const bf16_t*)a.dO, L, wave, lane);
+  TileDma<D, BM, 4> qdma((const e16_t*)a.q, L, wave, lane);
+  TileDma<D, BM, 4> odma((const e16_t*)a.dO, L, wave, lane);
   const float* lse2_h = a.lse2;
   const float* delta_h = a.delta;
   // Stage st: Q tile, dO tile, then lse2[BM] and delta[BM] of the same rows.
@@ -196,12 +196,12 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     vec64_dma(lds_base(st ? st1_ : st0_) + odd * (BM * 4), odd ? delta_h : lse2_h, L, q0, lane);
   };
 
-  bf16x8 kreg[DS], vreg[DS];
+  e16x8 kreg[DS], vreg[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds) {
     const size_t off = (size_t)key * D + ds * 16 + hi * 8;
-    kreg[ds] = as_bf16x8(key < L ? gload16(Kh + off) : zero4);
-    vreg[ds] = as_bf16x8(key < L ? gload16(Vh + off) : zero4);
+    kreg[ds] = as_e16x8(key < L ? gload16(Kh + off) : zero4);
+    vreg[ds] = as_e16x8(key < L ? gload16(Vh + off) : zero4);
   }
   const TileAddr<D> ad(lane);
 
@@ -228,7 +228,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
 
     // Exponentials and dS of sub-block sb; also packs P and dS to bf16.
     auto softmax_grad = [&](int sb, f32x16& s, f32x16& dp, const f32x4* l4, const f32x4* d4,
-                            bf16x8* pb, bf16x8* gb) {
+                            e16x8* pb, e16x8* gb) {
       // Element i is query qt0 + sb*32 + hi*4 + c (c = (i/4)*8 + i%4) against this
       // lane's key; causally visible iff c >= lo.
       const int lo = key - (qt0 + sb * 32) - hi * 4;
@@ -244,8 +244,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
         }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        pb[h] = pack8(s, h);
-        gb[h] = pack8(dp, h);
+        pb[h] = pack8<F16>(s, h);
+        gb[h] = pack8<F16>(dp, h);
       }
     };
     auto read_stats = [&](int sb, f32x4* l4, f32x4* d4) {
@@ -256,7 +256,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
         d4[g] = *(const ATTN_LDS f32x4*)(del_t + rl * 4);
       }
     };
-    auto read_tr = [&](int sb, bf16x8 (*qo)[2]) {  // qo[h*DB + db] = {dO^T, Q^T}
+    auto read_tr = [&](int sb, e16x8 (*qo)[2]) {  // qo[h*DB + db] = {dO^T, Q^T}
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -265,13 +265,13 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
           qo[h * DB + db][1] = ad.trop(Qt, sb * 32 + h * 16, db);
         }
     };
-    auto grad_mfma = [&](bf16x8 (*qo)[2], const bf16x8* pb, const bf16x8* gb) {
+    auto grad_mfma = [&](e16x8 (*qo)[2], const e16x8* pb, const e16x8* gb) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dv[db] = mfma32x32x16(qo[h * DB + db][0], pb[h], dv[db]);
-          dk[db] = mfma32x32x16(qo[h * DB + db][1], gb[h], dk[db]);
+          dv[db] = mfma32x32x16<F16>(qo[h * DB + db][0], pb[h], dv[db]);
+          dk[db] = mfma32x32x16<F16>(qo[h * DB + db][1], gb[h], dk[db]);
         }
     };
 
@@ -281,7 +281,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     // read is issued a phase ahead of the MFMA that consumes it.
     constexpr int PM = 2 * DS;  // MFMAs per phase
     // Phase 1a: Q/dO row operands of A.
-    bf16x8 qa[DS], oa[DS];
+    e16x8 qa[DS], oa[DS];
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       qa[ds] = ad.rowop(Qt, 0, ds);
@@ -289,14 +289,14 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // Phase 1b: S_A = Q_A K^T, dP_A = dO_A V^T; reads: row operands of B, stats of A.
-    f32x16 sA = mfma32x32x16_z(qa[0], kreg[0]);
-    f32x16 dpA = mfma32x32x16_z(oa[0], vreg[0]);
+    f32x16 sA = mfma32x32x16_z<F16>(qa[0], kreg[0]);
+    f32x16 dpA = mfma32x32x16_z<F16>(oa[0], vreg[0]);
 #pragma unroll
     for (int ds = 1; ds < DS; ++ds) {
-      sA = mfma32x32x16(qa[ds], kreg[ds], sA);
-      dpA = mfma32x32x16(oa[ds], vreg[ds], dpA);
+      sA = mfma32x32x16<F16>(qa[ds], kreg[ds], sA);
+      dpA = mfma32x32x16<F16>(oa[ds], vreg[ds], dpA);
     }
-    bf16x8 qb[DS], ob[DS];
+    e16x8 qb[DS], ob[DS];
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       qb[ds] = ad.rowop(Qt, 32, ds);
@@ -311,18 +311,18 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // Phase 2: S_B, dP_B; VALU of A; reads: stats of B, transposed operands of A.
-    f32x16 sB = mfma32x32x16_z(qb[0], kreg[0]);
-    f32x16 dpB = mfma32x32x16_z(ob[0], vreg[0]);
+    f32x16 sB = mfma32x32x16_z<F16>(qb[0], kreg[0]);
+    f32x16 dpB = mfma32x32x16_z<F16>(ob[0], vreg[0]);
 #pragma unroll
     for (int ds = 1; ds < DS; ++ds) {
-      sB = mfma32x32x16(qb[ds], kreg[ds], sB);
-      dpB = mfma32x32x16(ob[ds], vreg[ds], dpB);
+      sB = mfma32x32x16<F16>(qb[ds], kreg[ds], sB);
+      dpB = mfma32x32x16<F16>(ob[ds], vreg[ds], dpB);
     }
-    bf16x8 pA[2], gA[2];
+    e16x8 pA[2], gA[2];
     softmax_grad(0, sA, dpA, lA, dA, pA, gA);
     f32x4 lB[4], dB[4];
     read_stats(1, lB, dB);
-    bf16x8 trA[2 * DB][2];
+    e16x8 trA[2 * DB][2];
     read_tr(0, trA);
 #pragma unroll
     for (int i = 0; i < PM; ++i) {
@@ -333,9 +333,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     __builtin_amdgcn_sched_barrier(0);
     // Phase 3: dV, dK += sub-block A; VALU of B; reads: transposed operands of B.
     grad_mfma(trA, pA, gA);
-    bf16x8 pB[2], gB[2];
+    e16x8 pB[2], gB[2];
     softmax_grad(1, sB, dpB, lB, dB, pB, gB);
-    bf16x8 trB[2 * DB][2];
+    e16x8 trB[2 * DB][2];
     read_tr(1, trB);
 #pragma unroll
     for (int i = 0; i < PM; ++i) {
@@ -350,32 +350,44 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     __syncthreads();
   };
 
-  for (int g = 0; g < G; ++g) {
+  // Heads of the group one after another; the causal diagonal pairs of all
+  // heads run first and the unmasked tiles after, so each loop body holds one
+  // variant of the tile code (with both in one loop the register allocator
+  // went past its budget and spilled).
+  auto set_head = [&](int g) {
     const size_t qoff = (size_t)(hq0 + g) * N;
-    qdma.head = (const bf16_t*)a.q + qoff * D;
-    odma.head = (const bf16_t*)a.dO + qoff * D;
+    qdma.head = (const e16_t*)a.q + qoff * D;
+    odma.head = (const e16_t*)a.dO + qoff * D;
     lse2_h = a.lse2 + qoff;
     delta_h = a.delta + qoff;
-    // Stage 0 is free: every wave passed the barrier that ended the previous
-    // head's last tile.
-    load_tile(q_begin, 0);
-    dma_wait();
-    __syncthreads();
-    int t = 0;
-    if (CAUSAL) {  // query tiles [n0, n0 + 128): the diagonal
+  };
+  // Every loop iteration starts by filling stage 0, which is free: every wave
+  // passed the barrier that ended the previous tile.
+  if (CAUSAL) {  // query tiles [n0, n0 + 128): the diagonal
+    for (int g = 0; g < G; ++g) {
+      set_head(g);
+      load_tile(q_begin, 0);
+      dma_wait();
+      __syncthreads();
       step(0, 0, true);
       step(1, 1, true);
-      t = 2;
     }
-    for (; t < nqt; t += 2) {
+  }
+  const int t0 = CAUSAL ? 2 : 0;
+  for (int g = 0; g < G; ++g) {
+    set_head(g);
+    load_tile(q_begin + t0 * BM, 0);
+    dma_wait();
+    __syncthreads();
+    for (int t = t0; t < nqt; t += 2) {
       step(t, 0, false);
       step(t + 1, 1, false);
     }
   }
 
   if (key < N) {
-    store_rowT<DB>(dKh + (size_t)key * D, dk, a.scale, key < L, hi);
-    store_rowT<DB>(dVh + (size_t)key * D, dv, 1.f, key < L, hi);
+    store_rowT<DB, F16>(dKh + (size_t)key * D, dk, a.scale, key < L, hi);
+    store_rowT<DB, F16>(dVh + (size_t)key * D, dv, 1.f, key < L, hi);
   }
 }
 
@@ -387,7 +399,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
 //   dS^T = P^T o (dP^T - delta)   (LSE and delta are per-lane scalars)
 //   dQ^T (d x q)  += K^T dS^T  A = K^T (transposing LDS read), B = dS^T
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   constexpr int BM = 128, BN = 64;
   constexpr int TILE = BN * D * 2;
@@ -407,9 +419,9 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   const int m0 = mt * BM;
   const size_t hoff = (size_t)bh * N * D;
   const size_t kvoff = (size_t)((bh / a.H) * a.H_kv + (bh % a.H) / (a.H / a.H_kv)) * N * D;
-  const bf16_t* __restrict__ Qh = (const bf16_t*)a.q + hoff;
-  const bf16_t* __restrict__ dOh = (const bf16_t*)a.dO + hoff;
-  bf16_t* __restrict__ dQh = (bf16_t*)a.dq + hoff;
+  const e16_t* __restrict__ Qh = (const e16_t*)a.q + hoff;
+  const e16_t* __restrict__ dOh = (const e16_t*)a.dO + hoff;
+  e16_t* __restrict__ dQh = (e16_t*)a.dq + hoff;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
   if (m0 >= L) {
@@ -428,19 +440,19 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   const int nt = ((kv_end + BN - 1) / BN + 1) & ~1;
   const float c2 = a.scale_log2;
 
-  const TileDma<D, BN, 4> kdma((const bf16_t*)a.k + kvoff, L, wave, lane);
-  const TileDma<D, BN, 4> vdma((const bf16_t*)a.v + kvoff, L, wave, lane);
+  const TileDma<D, BN, 4> kdma((const e16_t*)a.k + kvoff, L, wave, lane);
+  const TileDma<D, BN, 4> vdma((const e16_t*)a.v + kvoff, L, wave, lane);
   kdma.load(lds_base(k0_), 0);
   vdma.load(lds_base(v0_), 0);
 
   const float lse2 = qvalid ? a.lse2[(size_t)bh * N + q] : 0.f;
   const float dq_delta = qvalid ? a.delta[(size_t)bh * N + q] : 0.f;
-  bf16x8 qreg[DS], doreg[DS];
+  e16x8 qreg[DS], doreg[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds) {
     const size_t off = (size_t)q * D + ds * 16 + hi * 8;
-    qreg[ds] = as_bf16x8(qvalid ? gload16(Qh + off) : zero4);
-    doreg[ds] = as_bf16x8(qvalid ? gload16(dOh + off) : zero4);
+    qreg[ds] = as_e16x8(qvalid ? gload16(Qh + off) : zero4);
+    doreg[ds] = as_e16x8(qvalid ? gload16(dOh + off) : zero4);
   }
   const TileAddr<D> ad(lane);
 
@@ -467,7 +479,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
     const lds_t* Kt = lds_base(st ? k1_ : k0_);
     const lds_t* Vt = lds_base(st ? v1_ : v0_);
 
-    auto softmax_grad = [&](int kb, const f32x16& s, f32x16& dp, bf16x8* gb) {
+    auto softmax_grad = [&](int kb, const f32x16& s, f32x16& dp, e16x8* gb) {
       // Element i is key n0 + kb*32 + hi*4 + c (c = (i/4)*8 + i%4) against this
       // lane's query; it is visible iff c <= lim.
       const int lim = (CAUSAL ? min(q, L - 1) : L - 1) - n0 - kb * 32 - hi * 4;
@@ -477,32 +489,32 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
         if (MASKED) p = ((i >> 2) * 8 + (i & 3)) <= lim ? p : 0.f;
         dp[i] = p * (dp[i] - dq_delta);
       }
-      gb[0] = pack8(dp, 0);
-      gb[1] = pack8(dp, 1);
+      gb[0] = pack8<F16>(dp, 0);
+      gb[1] = pack8<F16>(dp, 1);
     };
-    auto read_tr = [&](int kb, bf16x8* kt) {
+    auto read_tr = [&](int kb, e16x8* kt) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int db = 0; db < DB; ++db) kt[h * DB + db] = ad.trop(Kt, kb * 32 + h * 16, db);
     };
-    auto dq_mfma = [&](const bf16x8* kt, const bf16x8* gb) {
+    auto dq_mfma = [&](const e16x8* kt, const e16x8* gb) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16(kt[h * DB + db], gb[h], acc[db]);
+        for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16<F16>(kt[h * DB + db], gb[h], acc[db]);
     };
 
     // Operands are read just ahead of their MFMAs (two waves per SIMD cover
     // the LDS latency; a deeper lookahead would not fit in 256 VGPRs).
     constexpr int PM = 2 * DS;  // score MFMAs per key block
     auto scores = [&](int kb, f32x16& s, f32x16& dp) {
-      s = mfma32x32x16_z(ad.rowop(Kt, kb * 32, 0), qreg[0]);
-      dp = mfma32x32x16_z(ad.rowop(Vt, kb * 32, 0), doreg[0]);
+      s = mfma32x32x16_z<F16>(ad.rowop(Kt, kb * 32, 0), qreg[0]);
+      dp = mfma32x32x16_z<F16>(ad.rowop(Vt, kb * 32, 0), doreg[0]);
 #pragma unroll
       for (int ds = 1; ds < DS; ++ds) {
-        s = mfma32x32x16(ad.rowop(Kt, kb * 32, ds), qreg[ds], s);
-        dp = mfma32x32x16(ad.rowop(Vt, kb * 32, ds), doreg[ds], dp);
+        s = mfma32x32x16<F16>(ad.rowop(Kt, kb * 32, ds), qreg[ds], s);
+        dp = mfma32x32x16<F16>(ad.rowop(Vt, kb * 32, ds), doreg[ds], dp);
       }
     };
     // Phase 1: S^T, dP^T of block 0.
@@ -518,7 +530,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
     // Phase 2: S^T, dP^T of block 1; VALU of block 0.
     f32x16 s1, dp1;
     scores(1, s1, dp1);
-    bf16x8 g0[2];
+    e16x8 g0[2];
     softmax_grad(0, s0, dp0, g0);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -529,10 +541,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // Phase 3: dQ^T += K^T dS^T of block 0; VALU of block 1.
-    bf16x8 kt0[2 * DB];
+    e16x8 kt0[2 * DB];
     read_tr(0, kt0);
     dq_mfma(kt0, g0);
-    bf16x8 g1[2];
+    e16x8 g1[2];
     softmax_grad(1, s1, dp1, g1);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -543,7 +555,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // Phase 4: dQ^T += K^T dS^T of block 1.
-    bf16x8 kt1[2 * DB];
+    e16x8 kt1[2 * DB];
     read_tr(1, kt1);
     dq_mfma(kt1, g1);
     dma_wait();
@@ -560,44 +572,50 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   step(j, 0, true);
   step(j + 1, 1, true);
 
-  if (q < N) store_rowT<DB>(dQh + (size_t)q * D, acc, a.scale, qvalid, hi);
+  if (q < N) store_rowT<DB, F16>(dQh + (size_t)q * D, acc, a.scale, qvalid, hi);
 }
 
 // Thin __global__ wrappers: with the buffer builtins inside a __global__
 // template body, the host pass dropped some of the launch stubs.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdArgs a) {
-  bwd_dkdv_body<D, CAUSAL>(a);
+  bwd_dkdv_body<D, CAUSAL, F16>(a);
 }
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
-  bwd_dq_body<D, CAUSAL>(a);
+  bwd_dq_body<D, CAUSAL, F16>(a);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const long long rows = (long long)a.B * a.H * a.N;
   constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_pre_kernel<D, F16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int heads = a.B * a.H;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, F16>),
                      dim3((unsigned)(a.B * a.H_kv * ((a.N + 127) / 128))),
                      dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(heads * ((a.N + 127) / 128))),
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, F16>), dim3((unsigned)(heads * ((a.N + 127) / 128))),
                      dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
+template <bool F16>
+hipError_t launch_bwd_fmt(const BwdArgs& a, int d, bool causal, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_bwd_t<64, true, F16>(a, stream) : launch_bwd_t<64, false, F16>(a, stream);
+  return causal ? launch_bwd_t<128, true, F16>(a, stream) : launch_bwd_t<128, false, F16>(a, stream);
+}
+
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int d, bool causal, hipStream_t stream) {
-  if (d == 64) return causal ? launch_bwd_t<64, true>(a, stream) : launch_bwd_t<64, false>(a, stream);
-  return causal ? launch_bwd_t<128, true>(a, stream) : launch_bwd_t<128, false>(a, stream);
+hipError_t launch_bwd_16(const BwdArgs& a, int d, bool causal, bool f16, hipStream_t stream) {
+  return f16 ? launch_bwd_fmt<true>(a, d, causal, stream) : launch_bwd_fmt<false>(a, d, causal, stream);
 }
 
 }  // namespace attn

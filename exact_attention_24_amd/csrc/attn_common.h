@@ -1,6 +1,6 @@
 // Device helpers shared by the gfx950 attention kernels: vector types, MFMA
 // wrappers, LDS access through address-space-3 pointers, lane exchanges and
-// bf16 packing. Everything here is written for CDNA4 (wave64, gfx950) only.
+// 16-bit packing. Everything here is written for CDNA4 (wave64, gfx950) only.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -10,9 +10,13 @@ namespace attn {
 
 #define ATTN_LDS __attribute__((address_space(3)))
 
-typedef __bf16 bf16_t;
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+// 16-bit elements: bf16 or fp16 (the kernels take the format as a template
+// flag F16; storage, LDS layout and loads are the same for both).
+typedef uint16_t e16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 e16x8;  // MFMA operand
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
@@ -27,21 +31,28 @@ constexpr float kLn2 = 0.6931471805599453f;
 // factor underflows to 0 instead of forming (-inf) - (-inf).
 constexpr float kMaxInit = -1.0e30f;
 
-// D += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.
-// A: lane l holds row l%32, k = 8*(l/32) .. +7.  B: lane l holds column l%32,
-// k = 8*(l/32) .. +7.  D: lane l holds column l%32, rows (i/4)*8 + 4*(l/32) + i%4.
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// D += A(32x16) * B(16x32), 16-bit inputs (bf16, or fp16 when F16), fp32
+// accumulate. A: lane l holds row l%32, k = 8*(l/32) .. +7.  B: lane l holds
+// column l%32, k = 8*(l/32) .. +7.  D: lane l holds column l%32, rows
+// (i/4)*8 + 4*(l/32) + i%4. Both formats use the same lane layout.
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32x32x16(e16x8 a, e16x8 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 // Same product with a zero accumulator (no VGPRs need clearing first).
-__device__ __forceinline__ f32x16 mfma32x32x16_z(bf16x8 a, bf16x8 b) {
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32x32x16_z(e16x8 a, e16x8 b) {
   const f32x16 z = {};
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, z, 0, 0, 0);
+  return mfma32x32x16<F16>(a, b, z);
 }
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ e16x8 as_e16x8(u32x4 v) { return __builtin_bit_cast(e16x8, v); }
 
 // ---- LDS access (address space 3, so the compiler emits ds_* instructions)
 __device__ __forceinline__ lds_t* lds_base(char* generic) { return (lds_t*)generic; }
@@ -61,9 +72,9 @@ __device__ __forceinline__ u32x2 lds_load_tr16(const lds_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-__device__ __forceinline__ bf16x8 join_bf16x8(u32x2 lo, u32x2 hi) {
+__device__ __forceinline__ e16x8 join_e16x8(u32x2 lo, u32x2 hi) {
   u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
-  return as_bf16x8(v);
+  return as_e16x8(v);
 }
 
 // ---- global access
@@ -94,15 +105,29 @@ __device__ __forceinline__ float sum_halves(float x) {
   return lo + hi;
 }
 
-// ---- bf16 packing: one v_cvt_pk_bf16_f32 (round to nearest even) per pair
+// ---- 16-bit packing: one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 (round to
+// nearest even) per pair
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   const f32x2_t v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  if constexpr (F16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+// The two 16-bit values of a 32-bit word, widened exactly to fp32.
+template <bool F16>
+__device__ __forceinline__ float unpack_lo(uint32_t u) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+  else return __builtin_bit_cast(float, u << 16);
+}
+template <bool F16>
+__device__ __forceinline__ float unpack_hi(uint32_t u) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+  else return __builtin_bit_cast(float, u & 0xffff0000u);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

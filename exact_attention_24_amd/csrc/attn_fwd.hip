@@ -52,8 +52,8 @@ namespace {
 // ----------------------------------------------------------------------------
 constexpr float kLazyRescale = 8.0f;  // log2 of the largest unnormalised weight
 
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
+template <int D, bool CAUSAL, bool F16>
+__device__ __forceinline__ void fwd_16_body(const FwdArgs& a) {
   constexpr int BM = 128, BN = 64;
   constexpr int TILE = BN * D * 2;
   constexpr int CH = D / 8;           // 16-byte chunks per row
@@ -81,8 +81,8 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   const size_t hoff = (size_t)bh * N * D;
   // Grouped K/V heads: query head h reads K/V head h / (H / H_kv).
   const size_t kvoff = (size_t)(b * a.H_kv + (bh % a.H) / (a.H / a.H_kv)) * N * D;
-  const bf16_t* __restrict__ Qh = (const bf16_t*)a.q + hoff;
-  bf16_t* __restrict__ Oh = (bf16_t*)a.o + hoff;
+  const e16_t* __restrict__ Qh = (const e16_t*)a.q + hoff;
+  e16_t* __restrict__ Oh = (e16_t*)a.o + hoff;
   float* __restrict__ lse_h = a.lse ? a.lse + (size_t)bh * N : nullptr;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
@@ -102,16 +102,16 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   const int w_end = (qw >= L) ? 0 : (CAUSAL ? min(L, qw + 32) : L);
   const int wnt = (w_end + BN - 1) / BN;                 // tiles this wave computes
 
-  const TileDma<D, BN, 4> kdma((const bf16_t*)a.k + kvoff, N, wave, lane);
-  const TileDma<D, BN, 4> vdma((const bf16_t*)a.v + kvoff, N, wave, lane);
+  const TileDma<D, BN, 4> kdma((const e16_t*)a.k + kvoff, N, wave, lane);
+  const TileDma<D, BN, 4> vdma((const e16_t*)a.v + kvoff, N, wave, lane);
   kdma.load(kst[0], 0);
   vdma.load(vst[0], 0);
 
   // Q rows -> VGPRs, B-operand layout: lane holds query q, d = 16*ds + 8*hi .. +7.
-  bf16x8 qr[DS];
+  e16x8 qr[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds)
-    qr[ds] = as_bf16x8(q < N ? gload16(Qh + (size_t)q * D + ds * 16 + hi * 8) : zero4);
+    qr[ds] = as_e16x8(q < N ? gload16(Qh + (size_t)q * D + ds * 16 + hi * 8) : zero4);
 
   f32x16 o[DB];
 #pragma unroll
@@ -134,12 +134,12 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
       const lds_t* kt = kst[ST];
       const lds_t* vt = vst[ST];
       // S^T (64 keys x 32 queries) as two 32x32 blocks.
-      f32x16 s0 = mfma32x32x16_z(row_operand<D>(kt, 0, 0, lane), qr[0]);
-      f32x16 s1 = mfma32x32x16_z(row_operand<D>(kt, 32, 0, lane), qr[0]);
+      f32x16 s0 = mfma32x32x16_z<F16>(row_operand<D>(kt, 0, 0, lane), qr[0]);
+      f32x16 s1 = mfma32x32x16_z<F16>(row_operand<D>(kt, 32, 0, lane), qr[0]);
 #pragma unroll
       for (int ds = 1; ds < DS; ++ds) {
-        s0 = mfma32x32x16(row_operand<D>(kt, 0, ds * 2, lane), qr[ds], s0);
-        s1 = mfma32x32x16(row_operand<D>(kt, 32, ds * 2, lane), qr[ds], s1);
+        s0 = mfma32x32x16<F16>(row_operand<D>(kt, 0, ds * 2, lane), qr[ds], s0);
+        s1 = mfma32x32x16<F16>(row_operand<D>(kt, 32, ds * 2, lane), qr[ds], s1);
       }
       // Keep several K operand reads in flight ahead of the score MFMAs.
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
@@ -185,13 +185,13 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
       }
       l_part += sa + sb;
       // P^T -> bf16 B operands, one per 16-key step.
-      const bf16x8 pb[4] = {pack8(s0, 0), pack8(s0, 1), pack8(s1, 0), pack8(s1, 1)};
+      const e16x8 pb[4] = {pack8<F16>(s0, 0), pack8<F16>(s0, 1), pack8<F16>(s1, 0), pack8<F16>(s1, 1)};
       // O^T (D x 32) += V^T (D x 64) P^T (64 x 32).
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          o[db] = mfma32x32x16(tr_operand<D>(vt, ks * 16, db * 32, lane), pb[ks], o[db]);
+          o[db] = mfma32x32x16<F16>(tr_operand<D>(vt, ks * 16, db * 32, lane), pb[ks], o[db]);
       // Transposed V reads: eight in flight ahead of the P V MFMAs.
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
 #pragma unroll
@@ -216,13 +216,13 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   const bool valid = q < L && l_tot > 0.f;
   const float inv = valid ? 1.f / l_tot : 0.f;
   if (q < N) {
-    bf16_t* orow = Oh + (size_t)q * D;
+    e16_t* orow = Oh + (size_t)q * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const u32x2 w = {pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
-                         pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+        const u32x2 w = {pack2<F16>(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
+                         pack2<F16>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
         gstore8(orow + db * 32 + g * 8 + hi * 4, w);
       }
     if (lse_h && hi == 0) lse_h[q] = valid ? m_ref * a.scale + logf(l_tot) : -INFINITY;
@@ -233,9 +233,9 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
 // host compilation pass emits every instantiation's launch stub (with the
 // buffer-load builtins directly in a __global__ template body it silently
 // dropped some of them).
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
-  fwd_bf16_body<D, CAUSAL>(a);
+template <int D, bool CAUSAL, bool F16>
+__global__ void __launch_bounds__(256, 2) fwd_16_kernel(FwdArgs a) {
+  fwd_16_body<D, CAUSAL, F16>(a);
 }
 
 // ----------------------------------------------------------------------------
@@ -337,13 +337,20 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t stream) {
+template <int D, bool CAUSAL, bool F16>
+hipError_t launch_16_t(const FwdArgs& a, hipStream_t stream) {
   constexpr int BM = 128;
   const int nm = (a.N + BM - 1) / BM;
   dim3 grid((unsigned)(nm * a.B * a.H)), block(256);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL((fwd_16_kernel<D, CAUSAL, F16>), grid, block, 0, stream, a);
   return hipGetLastError();
+}
+
+template <bool F16>
+hipError_t launch_16_fmt(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_16_t<64, true, F16>(a, stream) : launch_16_t<64, false, F16>(a, stream);
+  return causal ? launch_16_t<128, true, F16>(a, stream) : launch_16_t<128, false, F16>(a, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -356,9 +363,8 @@ hipError_t launch_f32_t(const FwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
-  if (d == 64) return causal ? launch_bf16_t<64, true>(a, stream) : launch_bf16_t<64, false>(a, stream);
-  return causal ? launch_bf16_t<128, true>(a, stream) : launch_bf16_t<128, false>(a, stream);
+hipError_t launch_fwd_16(const FwdArgs& a, int d, bool causal, bool f16, hipStream_t stream) {
+  return f16 ? launch_16_fmt<true>(a, d, causal, stream) : launch_16_fmt<false>(a, d, causal, stream);
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream) {

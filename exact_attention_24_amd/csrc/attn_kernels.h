@@ -41,9 +41,10 @@ struct BwdArgs {
 };
 
 // Each launcher enqueues its kernels on `stream` and returns the launch status.
-hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+// 16-bit formats: bf16, or fp16 when f16 is set.
+hipError_t launch_fwd_16(const FwdArgs& a, int d, bool causal, bool f16, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_16(const BwdArgs& a, int d, bool causal, bool f16, hipStream_t stream);
 
 // Host-side mirror of the workgroup -> (head, row tile) order used by the
 // forward kernels (exposed for tests of the scheduling logic).

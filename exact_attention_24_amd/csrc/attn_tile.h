@@ -1,12 +1,12 @@
 // LDS tile layout and MFMA operand helpers shared by the forward and backward
-// kernels (gfx950, wave64, v_mfma_f32_32x32x16_bf16).
+// kernels (gfx950, wave64, v_mfma_f32_32x32x16_bf16 / _f16).
 #pragma once
 
 #include "attn_common.h"
 
 namespace attn {
 
-// A row-major [rows][D] bf16 tile in LDS, no padding; the 16-byte chunk c of
+// A row-major [rows][D] 16-bit tile in LDS, no padding; the 16-byte chunk c of
 // row r sits at chunk c ^ swz(r). The XOR keeps both read patterns free of
 // bank conflicts on gfx950's 64 LDS banks: 16 consecutive rows read at one
 // chunk (ds_read_b128 operands), and 4 consecutive rows read as 4 consecutive
@@ -32,8 +32,8 @@ __device__ __forceinline__ int tile_off_col(int r, int col) {
 // A operand (32 rows x 16 k) read straight from a tile: lane holds row
 // row0 + lane%32 and k = chunk*8 + 8*(lane/32) .. +7.
 template <int D>
-__device__ __forceinline__ bf16x8 row_operand(const lds_t* tile, int row0, int chunk, int lane) {
-  return as_bf16x8(lds_load16(tile + tile_off<D>(row0 + (lane & 31), chunk + (lane >> 5))));
+__device__ __forceinline__ e16x8 row_operand(const lds_t* tile, int row0, int chunk, int lane) {
+  return as_e16x8(lds_load16(tile + tile_off<D>(row0 + (lane & 31), chunk + (lane >> 5))));
 }
 
 // Transposed operand from a row-major tile T (rows = the contraction index):
@@ -46,20 +46,21 @@ __device__ __forceinline__ bf16x8 row_operand(const lds_t* tile, int row0, int c
 // pieces M[src] its group addressed, so lane src addresses row
 // row0 + hi*4 + (src>>2) at column col0 + 16*((lane>>4)&1) + 4*(src&3).
 template <int D>
-__device__ __forceinline__ bf16x8 tr_operand(const lds_t* tile, int row0, int col0, int lane) {
+__device__ __forceinline__ e16x8 tr_operand(const lds_t* tile, int row0, int col0, int lane) {
   const int r = row0 + (lane >> 5) * 4 + ((lane & 15) >> 2);
   const int col = col0 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
   const u32x2 lo = lds_load_tr16(tile + tile_off_col<D>(r, col));
   const u32x2 up = lds_load_tr16(tile + tile_off_col<D>(r + 8, col));
-  return join_bf16x8(lo, up);
+  return join_e16x8(lo, up);
 }
 
-// Accumulator values 8h .. 8h+7 packed to bf16 (round to nearest even): the
-// B operand for the 16-row k step h of the next product.
-__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int h) {
-  u32x4 w = {pack_bf16x2(s[8 * h + 0], s[8 * h + 1]), pack_bf16x2(s[8 * h + 2], s[8 * h + 3]),
-             pack_bf16x2(s[8 * h + 4], s[8 * h + 5]), pack_bf16x2(s[8 * h + 6], s[8 * h + 7])};
-  return as_bf16x8(w);
+// Accumulator values 8h .. 8h+7 packed to 16 bits (round to nearest even):
+// the B operand for the 16-row k step h of the next product.
+template <bool F16>
+__device__ __forceinline__ e16x8 pack8(const f32x16& s, int h) {
+  u32x4 w = {pack2<F16>(s[8 * h + 0], s[8 * h + 1]), pack2<F16>(s[8 * h + 2], s[8 * h + 3]),
+             pack2<F16>(s[8 * h + 4], s[8 * h + 5]), pack2<F16>(s[8 * h + 6], s[8 * h + 7])};
+  return as_e16x8(w);
 }
 
 // Direct global -> LDS tile loads (buffer_load_dwordx4 ... lds) for one
@@ -80,12 +81,12 @@ struct TileDma {
   static constexpr int ITER = ROWS / RPG / NWAVES;
   static_assert(ITER * RPG * NWAVES == ROWS, "tile rows must split evenly over the waves");
 
-  const bf16_t* head;
+  const e16_t* head;
   int n_rows;
   uint32_t voff[ITER];
   int wave;
 
-  __device__ __forceinline__ TileDma(const bf16_t* head_, int n_rows_, int wave_, int lane) {
+  __device__ __forceinline__ TileDma(const e16_t* head_, int n_rows_, int wave_, int lane) {
     head = head_;
     n_rows = n_rows_;
     wave = wave_;

@@ -71,8 +71,11 @@ typedef enum {
 
 typedef enum {
   ATTN_DTYPE_F32 = 0,  /* fp32 storage, fp32 arithmetic throughout */
-  ATTN_DTYPE_BF16 = 1  /* bf16 storage; products on bf16 MFMA with fp32 accumulation;
+  ATTN_DTYPE_BF16 = 1, /* bf16 storage; products on bf16 MFMA with fp32 accumulation;
                           softmax in fp32; outputs rounded to bf16 (nearest-even) */
+  ATTN_DTYPE_F16 = 2   /* fp16 storage, the same kernels on fp16 MFMA; P (<= 256 by the
+                          lazy rescale) and dS are rounded to fp16 before their
+                          products, so |dP - D| must stay below 65504 */
 } attn_dtype;
 
 /*
@@ -87,7 +90,7 @@ typedef enum {
  *  lse       [B,H,N] fp32, written; may be NULL when no backward will follow.
  *  B, H, N   >= 1.   d: 64 or 128 (ATTN_ERR_UNSUPPORTED otherwise).
  *
- * The bf16 forward is deterministic: the same inputs give bit-identical outputs.
+ * The 16-bit forwards are deterministic: the same inputs give bit-identical outputs.
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int N, int d, attn_dtype dtype, float scale, int causal,
@@ -126,7 +129,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype dtype);
  *  workspace        device buffer of at least attn_bwd_workspace_bytes(...)
  *                   bytes, 256-byte aligned; contents on entry are ignored.
  *  workspace_bytes  its size; smaller than required gives ATTN_ERR_INVALID_ARG.
- * Only ATTN_DTYPE_BF16 is implemented (ATTN_ERR_UNSUPPORTED for fp32).
+ * ATTN_DTYPE_BF16 and ATTN_DTYPE_F16 are implemented (ATTN_ERR_UNSUPPORTED for fp32).
  * Deterministic: no atomics are used.
  */
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,

@@ -61,8 +61,8 @@ __all__ = ["scores", "mask", "softmax_three_pass", "attn_ref_head", "kv_head", "
 
 
 def _f64(x) -> np.ndarray:
-    """Exact upcast to float64 (bf16 and fp32 values are representable)."""
-    if hasattr(x, "detach"):  # a torch tensor: go through fp32, which holds bf16 exactly
+    """Exact upcast to float64 (bf16, fp16 and fp32 values are representable)."""
+    if hasattr(x, "detach"):  # a torch tensor: go through fp32, which holds bf16/fp16 exactly
         import torch
         x = x.detach().to("cpu")
         if x.dtype in (torch.bfloat16, torch.float16):

@@ -44,7 +44,7 @@ def check_full(x, scale, causal, tag):
 
 # ------------------------------------------------------------ pinned page cases
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_hand_case(dtype, d, causal):
@@ -58,8 +58,10 @@ def test_hand_case(dtype, d, causal):
     o, lse = run_fwd(q, k, v, 1.0, causal)
     ro, rl = oracle.attn_ref_fwd(q, k, v, 1.0, causal)
     # bf16: O is in [4, 8), where half a bf16 ulp is 2^-6 = 0.0156, plus P rounded to
-    # bf16 before the P V product (relative 2^-9) times max|V| = 8: 0.0156
-    tol = 1e-5 if dtype == torch.float32 else 2 ** -6 + 2 ** -9 * 8
+    # bf16 before the P V product (relative 2^-9) times max|V| = 8: 0.0156.
+    # fp16: half an ulp in [4, 8) is 2^-9, P's relative rounding 2^-11.
+    tol = {torch.float32: 1e-5, torch.bfloat16: 2 ** -6 + 2 ** -9 * 8,
+           torch.float16: 2 ** -9 + 2 ** -11 * 8}[dtype]
     assert_close(o, ro, tol, "hand O")
     assert_close(lse, rl, LSE_TOL[dtype_name(q)], "hand LSE")
     assert torch.all(o[..., 2:] == 0)
@@ -82,7 +84,7 @@ def _one_hot_case(scores_by_key, values_by_key, N, d, dtype):
     return q.to(dtype), k.to(dtype), v.to(dtype)
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 def test_two_block_example(dtype):
     """[OpOpt] §三: blocks [1,2] and [3,1] in two different KV tiles merge to
     l = 2e^-2 + e^-1 + 1 ~= 1.638 relative to the max 3, so LSE = 3 + ln l."""
@@ -94,8 +96,10 @@ def test_two_block_example(dtype):
     assert abs(math.exp(float(lse[0, 0, 0]) - 3.0) - 1.638) <= 1e-3  # the page's printed value
     assert abs(float(lse[0, 0, 0]) - (3 + math.log(l))) <= LSE_TOL[dtype_name(q)]
     want = (0.5 * math.exp(-2) + 1.0 * math.exp(-1) + 1.5 + 2.0 * math.exp(-2)) / l
-    # bf16: O ~ 1.35, half an ulp in [1, 2) is 2^-8, plus 2^-9 * max|V| = 2^-8
-    tol = 1e-5 if dtype == torch.float32 else 2 ** -8 + 2 ** -9 * 2
+    # bf16: O ~ 1.35, half an ulp in [1, 2) is 2^-8, plus 2^-9 * max|V| = 2^-8;
+    # fp16: 2^-11 + 2^-11 * max|V|
+    tol = {torch.float32: 1e-5, torch.bfloat16: 2 ** -8 + 2 ** -9 * 2,
+           torch.float16: 2 ** -11 + 2 ** -11 * 2}[dtype]
     assert abs(float(o[0, 0, 0, 0]) - want) <= tol
 
 
@@ -123,7 +127,8 @@ SMALL = [  # (B, H, N, d) spanning several tiles with ragged tails
 ]
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16],
+                         ids=["bf16", "f32", "f16"])
 @pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
 def test_small_full(shape, causal, dtype):
@@ -132,7 +137,8 @@ def test_small_full(shape, causal, dtype):
     check_full(x, 1 / math.sqrt(d), causal, f"small{shape}")
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16],
+                         ids=["bf16", "f32", "f16"])
 @pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_small_varlen(d, causal, dtype):
@@ -179,6 +185,22 @@ def test_workload_sampled(name):
 
 
 # ------------------------------------------------------------- edge and stress
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_f16_large_values(d):
+    """fp16's range: Q, K scaled x8 (scores in the hundreds) and V x64 (|V| in
+    the hundreds, far above bf16 tests' magnitudes but well inside fp16): the
+    weights P stay <= 256 and O <= max|V|, so nothing overflows; compared with
+    the tolerance scaled by max|V|."""
+    x = make_inputs(1, 2, 300, d, torch.float16, seed=13)
+    big = make_inputs(1, 2, 300, d, torch.float16, seed=13, std=8.0)
+    x["q"], x["k"] = big["q"], big["k"]
+    x["v"] = (x["v"].float() * 64).to(torch.float16)
+    o, lse = run_fwd(x["q"], x["k"], x["v"], 1 / math.sqrt(d), True)
+    ro, rl = oracle.attn_ref_fwd(x["q"], x["k"], x["v"], 1 / math.sqrt(d), True)
+    assert_close(o, ro, O_TOL["f16"] * 64, "f16 large values O")
+    assert_close(lse, rl, LSE_TOL["f16"], "f16 large values LSE")
+
 
 def test_deterministic():
     x = make_inputs(2, 4, 1000, 128, torch.bfloat16, seed=5)

@@ -48,7 +48,8 @@ def _check_grads(got, ref, tag):
         assert e <= GRAD_REL_FRO, f"{tag} {name}: rel Frobenius err {e:.3e} > {GRAD_REL_FRO}"
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16],
+                         ids=["bf16", "f32", "f16"])
 @pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_gqa_forward(shape, causal, dtype):
