@@ -34,6 +34,8 @@ class Workload:
     one length per sequence, drawn uniformly from the range after the tensors.
     ``with_grad`` also draws the upstream gradient dO. ``H_kv`` (default H)
     gives K and V fewer heads than Q (grouped- or multi-query attention).
+    ``Nq`` (default N) makes a decode workload: Q holds the last Nq positions
+    of each sequence and K, V its N cached positions.
     """
 
     name: str
@@ -48,6 +50,7 @@ class Workload:
     with_grad: bool = False
     description: str = ""
     H_kv: Optional[int] = None
+    Nq: Optional[int] = None
 
     @property
     def kv_heads(self) -> int:
@@ -82,6 +85,14 @@ WORKLOADS = {
         Workload("causal_f16_b2_h32_n4096_d128", 2, 32, 4096, 128, "f16", True, 1007,
                  with_grad=True,
                  description="the causal B=2 H=32 N=4096 d=128 shape with fp16 inputs, fwd+bwd"),
+        Workload("decode_bf16_b8_h64_hkv8_nq1_nk8192_d128", 8, 64, 8192, 128, "bf16", True, 1008,
+                 H_kv=8, Nq=1,
+                 description="decode: one new token per sequence, 64 query heads over 8 K/V "
+                             "heads (the pages' 64:8 example), 8192 cached positions, bf16"),
+        Workload("decode_bf16_b8_h64_hkv8_nq8_nk8192_d128", 8, 64, 8192, 128, "bf16", True, 1009,
+                 H_kv=8, Nq=8, seqlen_range=(4096, 8192),
+                 description="decode of 8 new tokens per sequence (causal among themselves) "
+                             "over 4096..8192 cached positions, 64 query heads over 8 K/V heads"),
         Workload("gqa_causal_bf16_b2_h32_hkv8_n4096_d128", 2, 32, 4096, 128, "bf16", True, 1006,
                  with_grad=True, H_kv=8,
                  description="grouped-query attention, 32 query heads over 8 K/V heads (the "
@@ -102,25 +113,28 @@ def draw_seqlens(gen: torch.Generator, B: int, lo: int, hi: int) -> torch.Tensor
 def make_inputs(B: int, H: int, N: int, d: int, dtype: torch.dtype = torch.bfloat16,
                 seed: int = 0, with_grad: bool = False,
                 seqlen_range: Optional[tuple[int, int]] = None,
-                std: float = 1.0, H_kv: Optional[int] = None) -> dict:
+                std: float = 1.0, H_kv: Optional[int] = None, Nq: Optional[int] = None) -> dict:
     """Draw Q, K, V (and dO, then seqlens) on the CPU from one seeded generator.
 
     The draw order is fixed (Q, K, V, dO, seqlens) so a workload is the same
-    bits on every machine. K and V have H_kv heads (default H). Returns CPU
-    tensors in ``dtype``; ``seqlens`` is an int32 [B] tensor or None.
+    bits on every machine. K and V have H_kv heads (default H); Q (and dO)
+    have Nq rows (default N). Returns CPU tensors in ``dtype``; ``seqlens`` is
+    an int32 [B] tensor or None.
     """
     gen = torch.Generator(device="cpu")
     gen.manual_seed(int(seed))
     kv_heads = H if H_kv is None else H_kv
 
-    def draw(heads: int) -> torch.Tensor:
-        x = torch.randn((B, heads, N, d), generator=gen, dtype=torch.float32)
+    q_rows = N if Nq is None else Nq
+
+    def draw(heads: int, rows: int = N) -> torch.Tensor:
+        x = torch.randn((B, heads, rows, d), generator=gen, dtype=torch.float32)
         if std != 1.0:
             x = x * std
         return x.to(dtype).contiguous()
 
-    out = {"q": draw(H), "k": draw(kv_heads), "v": draw(kv_heads)}
-    out["do"] = draw(H) if with_grad else None
+    out = {"q": draw(H, q_rows), "k": draw(kv_heads), "v": draw(kv_heads)}
+    out["do"] = draw(H, q_rows) if with_grad else None
     out["seqlens"] = (draw_seqlens(gen, B, *seqlen_range)
                       if seqlen_range is not None else None)
     return out
@@ -128,4 +142,4 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: torch.dtype = torch.bfloa
 
 def make_workload_inputs(w: Workload) -> dict:
     return make_inputs(w.B, w.H, w.N, w.d, w.torch_dtype, w.seed, w.with_grad, w.seqlen_range,
-                       H_kv=w.H_kv)
+                       H_kv=w.H_kv, Nq=w.Nq)

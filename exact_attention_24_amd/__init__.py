@@ -15,7 +15,8 @@ import os
 import pathlib
 from typing import Optional
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string",
+__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode",
+           "attn_decode_workspace_bytes", "attn_status_string",
            "AttnError", "lib", "LIB_PATH", "DTYPE_F32", "DTYPE_BF16", "DTYPE_F16",
            "EXPORTED_SYMBOLS"]
 
@@ -27,7 +28,8 @@ DTYPE_BF16 = 1
 DTYPE_F16 = 2
 # Every function include/attn.h declares.
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_gqa", "attn_bwd", "attn_bwd_gqa",
-                    "attn_bwd_workspace_bytes", "attn_status_string", "attn_last_error")
+                    "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes",
+                    "attn_status_string", "attn_last_error")
 
 _lib = None
 
@@ -61,6 +63,11 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     L.attn_bwd_gqa.restype = i32
+    L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
+                              i32, vp, sz, vp]
+    L.attn_decode.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -217,3 +224,41 @@ def attn_bwd(q, k, v, o, do, lse, *, scale: Optional[float] = None, causal: bool
         st = lib().attn_bwd_gqa(*ptrs, B, H, H_kv, N, d, *tail)
         _check(st, "attn_bwd_gqa")
     return dq, dk, dv
+
+
+def attn_decode_workspace_bytes(B: int, H: int, H_kv: int, Nq: int, Nk: int, d: int,
+                                dtype_code: int = DTYPE_BF16, num_splits: int = 0) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d, dtype_code, num_splits))
+
+
+def attn_decode(q, k, v, *, scale: Optional[float] = None, causal: bool = False, kv_lens=None,
+                num_splits: int = 0, out=None, lse=None, workspace=None):
+    """Split-KV decode: q [B, H, Nq, d] (the last Nq positions of each sequence)
+    against k, v [B, H_kv, Nk, d]. Returns (O [B, H, Nq, d], LSE [B, H, Nq])."""
+    import torch
+    B, H, Nq, d = q.shape
+    dev = q.device
+    H_kv = _kv_heads(q, k)
+    Nk = k.shape[2]
+    _check_tensor("q", q, (B, H, Nq, d), q.dtype, dev)
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, (B, H_kv, Nk, d), q.dtype, dev)
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, (B, H, Nq, d), q.dtype, dev)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev) if lse is None else lse
+    _check_tensor("lse", lse, (B, H, Nq), torch.float32, dev)
+    need = attn_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d, code, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device buffer")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           B, H, H_kv, Nq, Nk, d, code, float(scale), int(bool(causal)),
+                           _seqlens_ptr(kv_lens, B, dev), int(num_splits), workspace.data_ptr(),
+                           nbytes, _stream_handle(dev))
+    _check(st, "attn_decode")
+    return out, lse

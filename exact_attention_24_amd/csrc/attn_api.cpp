@@ -43,6 +43,49 @@ attn_status check_heads(int H, int H_kv) {
   return ATTN_OK;
 }
 
+// Split plan of the decode: `splits` key ranges of `chunk_keys` keys (a
+// multiple of 32) per (batch, K/V head); 0 requested splits picks enough to
+// give about 2048 single-wave workgroups (at least 32 keys per split).
+struct DecodePlan {
+  int splits, chunk_keys, col_groups;
+};
+DecodePlan decode_plan(int B, int H, int H_kv, int Nq, int Nk, int num_splits) {
+  DecodePlan p;
+  p.col_groups = ((H / H_kv) * Nq + 31) / 32;
+  long long want = num_splits;
+  if (want <= 0) {
+    const long long units = (long long)B * H_kv * p.col_groups;
+    want = (2048 + units - 1) / units;
+  }
+  const long long max_splits = (Nk + 31) / 32;
+  if (want > max_splits) want = max_splits;
+  if (want < 1) want = 1;
+  const long long per = (Nk + want - 1) / want;
+  p.chunk_keys = (int)((per + 31) / 32 * 32);
+  p.splits = (Nk + p.chunk_keys - 1) / p.chunk_keys;
+  return p;
+}
+
+size_t decode_part_o_bytes(int B, int H, int Nq, int d, int splits) {
+  return (((size_t)B * H * Nq * splits * d * sizeof(float)) + 255) / 256 * 256;
+}
+
+attn_status check_decode(int B, int H, int H_kv, int Nq, int Nk, int d, attn_dtype dtype,
+                         int num_splits) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || num_splits < 0) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16)
+    return ATTN_ERR_INVALID_ARG;
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)Nk * d > 0x7fffffffLL || (long long)Nq * d > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  const DecodePlan p = decode_plan(B, H, H_kv, Nq, Nk, num_splits);
+  if ((long long)B * H_kv * p.col_groups * p.splits > 0x7fffffffLL ||
+      (long long)B * H * Nq > 0x7fffffffLL)
+    return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
 size_t attn_bwd_section_bytes(int B, int H, int N) {
   const size_t rows = (size_t)B * H * N;
   return ((rows * sizeof(float) + 255) / 256) * 256;
@@ -146,6 +189,46 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      float scale, int causal, const int32_t* seqlens, attn_stream_t stream) {
   return attn_bwd_gqa(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d,
                       dtype, scale, causal, seqlens, stream);
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d,
+                                   attn_dtype dtype, int num_splits) {
+  if (check_decode(B, H, H_kv, Nq, Nk, d, dtype, num_splits) != ATTN_OK) return 0;
+  const DecodePlan p = decode_plan(B, H, H_kv, Nq, Nk, num_splits);
+  const size_t ml = (((size_t)B * H * Nq * p.splits * 2 * sizeof(float)) + 255) / 256 * 256;
+  return decode_part_o_bytes(B, H, Nq, d, p.splits) + ml;
+}
+
+attn_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int H_kv, int Nq, int Nk, int d, attn_dtype dtype, float scale,
+                        int causal, const int32_t* kv_lens, int num_splits, void* workspace,
+                        size_t workspace_bytes, attn_stream_t stream) {
+  attn_status st = check_decode(B, H, H_kv, Nq, Nk, d, dtype, num_splits);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !o || !workspace) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(workspace, 256))
+    return ATTN_ERR_INVALID_ARG;
+  if ((lse && !aligned(lse, 4)) || (kv_lens && !aligned(kv_lens, 4))) return ATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < attn_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d, dtype, num_splits))
+    return ATTN_ERR_INVALID_ARG;
+  const DecodePlan p = decode_plan(B, H, H_kv, Nq, Nk, num_splits);
+  attn::DecArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.kv_lens = kv_lens;
+  a.part_o = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + decode_part_o_bytes(B, H, Nq, d, p.splits));
+  a.B = B; a.H = H; a.H_kv = H_kv; a.Nq = Nq; a.Nk = Nk;
+  a.splits = p.splits; a.chunk_keys = p.chunk_keys; a.col_groups = p.col_groups;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = attn::launch_decode_16(a, d, dtype == ATTN_DTYPE_F16, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    record_hip_error(e, "attn_decode launch");
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,221 @@
+// Split-KV decode for gfx950: a few new queries per sequence against a long
+// K/V cache.
+//
+// Pages cited (by title):
+//   [SafeSoftmax] "FlashAttention：从 Safe Softmax 到分块计算"
+//   [OpOpt]       "Attention 算子优化:从物化 N×N 矩阵到 FlashAttention 与 PagedAttention"
+//
+// Decode reads the whole K/V cache for very little arithmetic, so it is bound
+// by HBM bandwidth, not by the matrix cores ([OpOpt] §五). With one query row
+// per (batch, head) a forward-style launch would have B*H workgroups each
+// walking the full key range; here the key range of every K/V head is cut
+// into splits that run in parallel ([SafeSoftmax] §10: split the K/V
+// dimension across workgroups), each keeping the online-softmax state
+// (m, l, unnormalised O) of [SafeSoftmax] §3.1 for its keys, and a second
+// kernel combines the splits with the merge rule of [SafeSoftmax] §3.2.
+//
+// Split kernel: one wave per workgroup. The G = H / H_kv query heads that
+// share a K/V head ([OpOpt] §五) and their N_q queries are packed into the 32
+// columns of one MFMA block (column c = g*N_q + i), so each K/V byte is read
+// from HBM once for all of them. K/V chunks of 32 keys stream through a
+// per-wave double buffer in LDS by direct buffer->LDS loads; S^T = K Q^T and
+// O^T += V^T P^T run on v_mfma_f32_32x32x16 exactly as in the forward kernel.
+//
+// Query positions: the N_q queries of sequence b are its last N_q positions,
+// L_b - N_q .. L_b - 1, so with causal masking query i sees keys
+// j <= L_b - N_q + i (when N_q = L_b this is the forward's top-left mask).
+#include "attn_common.h"
+#include "attn_kernels.h"
+#include "attn_tile.h"
+
+#include <math.h>
+
+namespace attn {
+
+namespace {
+
+constexpr float kLazyRescaleDec = 8.0f;  // log2 of the largest unnormalised weight
+
+template <int D, bool F16>
+__device__ __forceinline__ void decode_split_body(const DecArgs& a) {
+  constexpr int BN = 32;  // keys per chunk
+  constexpr int TILE = BN * D * 2;
+  constexpr int DS = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char k0_[TILE], v0_[TILE], k1_[TILE], v1_[TILE];
+
+  const int lane = threadIdx.x, l32 = lane & 31, hi = lane >> 5;
+  const int G = a.H / a.H_kv;
+  int bid = blockIdx.x;
+  const int s = bid % a.splits;
+  bid /= a.splits;
+  const int cg = bid % a.col_groups;
+  bid /= a.col_groups;
+  const int bkv = bid;  // b * H_kv + kv head
+  const int b = bkv / a.H_kv, kvh = bkv % a.H_kv;
+  const int L = a.kv_lens ? min(max(a.kv_lens[b], 0), a.Nk) : a.Nk;
+
+  // This lane's query column.
+  const int col = cg * 32 + l32;
+  const bool cvalid = col < G * a.Nq;
+  const int g = cvalid ? col / a.Nq : 0, qi = cvalid ? col % a.Nq : 0;
+  const int h = kvh * G + g;
+  const size_t qrow = ((size_t)(b * a.H + h) * a.Nq + qi);  // row of q, o, lse, partials
+  const int pos = L - a.Nq + qi;                           // this query's position
+
+  const int j_begin = s * a.chunk_keys;
+  const int j_end = min(j_begin + a.chunk_keys, L);
+  const int nch = j_end > j_begin ? (j_end - j_begin + BN - 1) / BN : 0;
+
+  const size_t kvoff = (size_t)bkv * a.Nk * D;
+  const TileDma<D, BN, 1> kdma((const e16_t*)a.k + kvoff, j_end, 0, lane);
+  const TileDma<D, BN, 1> vdma((const e16_t*)a.v + kvoff, j_end, 0, lane);
+  if (nch > 0) {
+    kdma.load(lds_base(k0_), j_begin);
+    vdma.load(lds_base(v0_), j_begin);
+  }
+
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  e16x8 qr[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds)
+    qr[ds] = as_e16x8(cvalid ? gload16((const e16_t*)a.q + qrow * D + ds * 16 + hi * 8) : zero4);
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  float m_ref = kMaxInit, l_part = 0.f;
+  const float c2 = a.scale_log2;
+  // Last visible key of this column (keys past it are masked).
+  const int last = a.causal ? min(pos, L - 1) : L - 1;
+
+  auto chunk = [&](int t, const int st) {
+    const int j0 = j_begin + t * BN;
+    if (t + 1 < nch) {
+      kdma.load(lds_base(st ? k0_ : k1_), j0 + BN);
+      vdma.load(lds_base(st ? v0_ : v1_), j0 + BN);
+    }
+    const lds_t* Kt = lds_base(st ? k1_ : k0_);
+    const lds_t* Vt = lds_base(st ? v1_ : v0_);
+    f32x16 sc = mfma32x32x16_z<F16>(row_operand<D>(Kt, 0, 0, lane), qr[0]);
+#pragma unroll
+    for (int ds = 1; ds < DS; ++ds) sc = mfma32x32x16<F16>(row_operand<D>(Kt, 0, ds * 2, lane), qr[ds], sc);
+    // Element i is key j0 + hi*4 + c (c = (i/4)*8 + i%4); visible iff c <= lim.
+    const int lim = last - j0 - hi * 4;
+    if (__builtin_amdgcn_ballot_w64(lim < BN - 1)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = ((i >> 2) * 8 + (i & 3)) <= lim ? sc[i] : -INFINITY;
+    }
+    float mx = max3f(sc[0], sc[1], sc[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mx = max3f(mx, sc[i], sc[i + 1]);
+    mx = max_halves(fmaxf(mx, sc[15]));
+    if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c2 > kLazyRescaleDec)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = fast_exp2((m_ref - m_new) * c2);
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      m_ref = m_new;
+    }
+    const float mc = m_ref * c2;
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sc[i] = fast_exp2(fmaf(sc[i], c2, -mc));
+      sum += sc[i];
+    }
+    l_part += sum;
+    const e16x8 p0 = pack8<F16>(sc, 0), p1 = pack8<F16>(sc, 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      o[db] = mfma32x32x16<F16>(tr_operand<D>(Vt, 0, db * 32, lane), p0, o[db]);
+      o[db] = mfma32x32x16<F16>(tr_operand<D>(Vt, 16, db * 32, lane), p1, o[db]);
+    }
+    dma_wait();  // one wave: its own loads landing is all the next chunk needs
+  };
+  for (int t = 0; t < nch; t += 2) {
+    chunk(t, 0);
+    if (t + 1 < nch) chunk(t + 1, 1);
+  }
+
+  // Partial state of this split: m in log2 units (m_ref * scale * log2 e), the
+  // weight sum l and the unnormalised O, all relative to m. An empty split (or
+  // a column that saw no key) leaves l = 0, which the merge ignores.
+  const float l_tot = sum_halves(l_part);
+  if (cvalid) {
+    const size_t prow = qrow * a.splits + s;
+    float* po = a.part_o + prow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x4 w = {o[db][4 * gq + 0], o[db][4 * gq + 1], o[db][4 * gq + 2], o[db][4 * gq + 3]};
+        *(f32x4*)(po + db * 32 + gq * 8 + hi * 4) = w;
+      }
+    if (hi == 0) {
+      a.part_ml[2 * prow + 0] = l_tot > 0.f ? m_ref * c2 : -INFINITY;
+      a.part_ml[2 * prow + 1] = l_tot;
+    }
+  }
+}
+
+// Thin __global__ wrapper (the host pass drops launch stubs of __global__
+// templates whose body holds the buffer-load builtins directly).
+template <int D, bool F16>
+__global__ void __launch_bounds__(64) decode_split_kernel(DecArgs a) {
+  decode_split_body<D, F16>(a);
+}
+
+// Merge the splits of one query row ([SafeSoftmax] §3.2): with M = max_s m_s,
+// l = sum_s 2^(m_s - M) l_s and O = sum_s 2^(m_s - M) O_s / l; LSE = (M +
+// log2 l) ln 2. A row with l = 0 saw no key: O = 0, LSE = -inf.
+template <int D, bool F16>
+__global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
+  const size_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  const float* ml = a.part_ml + row * a.splits * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < a.splits; ++s)
+    if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
+  float l = 0.f, acc = 0.f;
+  if (M > -INFINITY) {
+    const float* po = a.part_o + row * a.splits * D + t;
+    for (int s = 0; s < a.splits; ++s) {
+      const float ls = ml[2 * s + 1];
+      if (ls > 0.f) {
+        const float w = fast_exp2(ml[2 * s] - M);
+        l += w * ls;
+        acc += w * po[(size_t)s * D];
+      }
+    }
+  }
+  const bool valid = l > 0.f;
+  const float out = valid ? acc / l : 0.f;
+  const uint32_t packed = pack2<F16>(out, 0.f);
+  ((uint16_t*)a.o)[row * D + t] = (uint16_t)(packed & 0xffffu);
+  if (t == 0 && a.lse) a.lse[row] = valid ? (M + log2f(l)) * kLn2 : -INFINITY;
+}
+
+template <int D, bool F16>
+hipError_t launch_decode_t(const DecArgs& a, hipStream_t stream) {
+  const unsigned wgs = (unsigned)(a.B * a.H_kv * a.col_groups * a.splits);
+  hipLaunchKernelGGL((decode_split_kernel<D, F16>), dim3(wgs), dim3(64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D, F16>), dim3((unsigned)(a.B * a.H * a.Nq)), dim3(D), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_16(const DecArgs& a, int d, bool f16, hipStream_t stream) {
+  if (d == 64) return f16 ? launch_decode_t<64, true>(a, stream) : launch_decode_t<64, false>(a, stream);
+  return f16 ? launch_decode_t<128, true>(a, stream) : launch_decode_t<128, false>(a, stream);
+}
+
+}  // namespace attn

@@ -40,11 +40,31 @@ struct BwdArgs {
   float scale_log2;
 };
 
+// Split-KV decode: q, o [B,H,Nq,D], k, v [B,H_kv,Nk,D], split kernel partials
+// in the workspace, merged into o and lse.
+struct DecArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;               // may be null
+  const int32_t* kv_lens;   // may be null (every sequence has Nk keys)
+  float* part_o;            // workspace: [B*H*Nq][splits][D] unnormalised partial O
+  float* part_ml;           // workspace: [B*H*Nq][splits][2] = (m * scale * log2 e, l)
+  int B, H, H_kv, Nq, Nk;
+  int splits;               // key-range splits per (batch, K/V head)
+  int chunk_keys;           // keys per split, a multiple of 32
+  int col_groups;           // ceil((H / H_kv) * Nq / 32) query-column blocks
+  int causal;
+  float scale, scale_log2;
+};
+
 // Each launcher enqueues its kernels on `stream` and returns the launch status.
 // 16-bit formats: bf16, or fp16 when f16 is set.
 hipError_t launch_fwd_16(const FwdArgs& a, int d, bool causal, bool f16, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_16(const BwdArgs& a, int d, bool causal, bool f16, hipStream_t stream);
+hipError_t launch_decode_16(const DecArgs& a, int d, bool f16, hipStream_t stream);
 
 // Host-side mirror of the workgroup -> (head, row tile) order used by the
 // forward kernels (exposed for tests of the scheduling logic).

@@ -24,7 +24,10 @@
  *  - the AIInfra FlashAttention note on dpshk.com: §2.1 (finite initial row
  *    max), §2.3 (dV = P^T dO, dS = P o (dP - rowsum(dP o P)), dP = dO V^T).
  *  - "Attention 算子优化..." §五 (grouped- and multi-query attention: several
- *    query heads share one K/V head).
+ *    query heads share one K/V head; decode reads the whole K/V cache per new
+ *    token and is bandwidth-bound).
+ *  - "FlashAttention：从 Safe Softmax 到分块计算" §10 (splitting the K/V range
+ *    across workgroups for decode, partial states combined by the §3.2 merge).
  *
  * Conventions shared by every entry point
  *  - Tensors are [B, H, N, d], contiguous, d fastest (element (b,h,i,c) sits at
@@ -150,6 +153,43 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, int B, int H, int H_kv, int N,
                          int d, attn_dtype dtype, float scale, int causal,
                          const int32_t* seqlens, attn_stream_t stream);
+
+/*
+ * attn_decode_workspace_bytes - device workspace attn_decode needs for these
+ * sizes and this num_splits (0 = automatic; the same value must be passed to
+ * attn_decode). It holds each split's partial state: fp32 O [B*H*Nq][splits][d]
+ * and (m, l) [B*H*Nq][splits][2]. Returns 0 for invalid or unsupported sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d,
+                                   attn_dtype dtype, int num_splits);
+
+/*
+ * attn_decode - split-KV attention for a few new queries against a long K/V
+ * cache (decode).
+ *
+ *  q         [B,H,Nq,d] of `dtype` (bf16 or fp16), read only.
+ *  k, v      [B,H_kv,Nk,d] of `dtype`, read only; query head h reads K/V head
+ *            h / (H / H_kv) as in attn_fwd_gqa.
+ *  o         [B,H,Nq,d] of `dtype`, written.
+ *  lse       [B,H,Nq] fp32 natural-log log-sum-exp, written; may be NULL.
+ *  kv_lens   optional DEVICE int32 [B]: sequence b has L_b valid keys (clamped
+ *            into [0, Nk]); NULL means Nk for every b.
+ *  causal    the Nq queries of sequence b are its last Nq positions,
+ *            L_b - Nq .. L_b - 1; with causal != 0 query i sees keys
+ *            j <= L_b - Nq + i (with Nq = L_b: the mask of attn_fwd), otherwise
+ *            every valid key. A query that sees no key gets O = 0, LSE = -inf.
+ *  num_splits  key-range splits per (batch, K/V head); 0 picks about 2048
+ *            workgroups' worth. Results do not depend on it beyond rounding.
+ *  workspace device buffer of attn_decode_workspace_bytes(...) bytes, 256-byte
+ *            aligned; contents on entry are ignored.
+ *
+ * Two launches on `stream`: the split kernel (partial softmax states) and the
+ * merge. fp32 and d outside {64, 128} return ATTN_ERR_UNSUPPORTED.
+ */
+attn_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int H_kv, int Nq, int Nk, int d, attn_dtype dtype,
+                        float scale, int causal, const int32_t* kv_lens, int num_splits,
+                        void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* attn_status_string(attn_status s);

@@ -46,6 +46,11 @@ Readings taken where the pages are silent (each is listed in the design notes):
     is the plain reading). In the backward a K/V head's gradient is the sum of
     the per-query-head gradients of its group (the chain rule through the
     shared tensor).
+  * Decode ([OpOpt] §五: each new token's query attends to the cached K, V of
+    all earlier tokens): the Nq queries of sequence b are its last Nq positions
+    L_b - Nq .. L_b - 1, so under the causal mask query i sees keys
+    j <= L_b - Nq + i (bottom-right alignment; for Nq = L_b it is the
+    forward's mask). Without the mask it sees every valid key.
   * Backward ([AIInfra] §2.3 gives dV = P^T dO and dS = P o (dP - rowsum(dP o P))
     with dP = dO V^T; the scale factor on dQ and dK is not on the pages and
     follows from S = scale * Q K^T by the chain rule):
@@ -57,7 +62,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["scores", "mask", "softmax_three_pass", "attn_ref_head", "kv_head", "attn_ref_fwd",
-           "attn_ref_rows", "attn_ref_bwd_head", "attn_ref_bwd"]
+           "attn_ref_rows", "attn_ref_decode", "attn_ref_bwd_head", "attn_ref_bwd"]
 
 
 def _f64(x) -> np.ndarray:
@@ -176,6 +181,30 @@ def attn_ref_fwd(q, k, v, scale: float, causal: bool = False, seqlens=None):
         for h in range(H):
             g = kv_head(h, H, H_kv)
             o[b, h], lse[b, h] = attn_ref_head(q[b, h], k[b, g], v[b, g], scale, causal, L)
+    return o, lse
+
+
+def attn_ref_decode(q, k, v, scale: float, causal: bool = False, kv_lens=None, heads=None):
+    """Decode: q [B, H, Nq, d] holds the last Nq positions of each sequence and
+    k, v [B, H_kv, Nk, d] its keys and values, sequence b having L_b valid keys
+    (kv_lens, default Nk). Steps 1-5 with row positions L_b - Nq + i.
+    Returns (O [B,H,Nq,d], LSE [B,H,Nq]) fp64; ``heads`` optionally restricts
+    the (b, h) pairs evaluated (the others are left 0)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Nq, _ = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    o = np.zeros((B, H, Nq, v.shape[-1]))
+    lse = np.zeros((B, H, Nq))
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in pairs:
+        L = _valid_len(kv_lens, b, Nk)
+        g = kv_head(h, H, H_kv)
+        pos = L - Nq + np.arange(Nq)
+        s = mask(scores(q[b, h], k[b, g], scale), pos, causal, L)
+        p, m, l = softmax_three_pass(s)
+        o[b, h] = p @ v[b, g]
+        with np.errstate(divide="ignore"):
+            lse[b, h] = np.where(l > 0.0, m + np.log(np.where(l > 0.0, l, 1.0)), -np.inf)
     return o, lse
 
 

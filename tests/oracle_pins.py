@@ -38,7 +38,8 @@ def oracle_impl():
     return types.SimpleNamespace(head=lambda *a, **kw: A.attn_ref_head(*a, **kw),
                                  bwd_head=lambda *a, **kw: A.attn_ref_bwd_head(*a, **kw),
                                  fwd=lambda *a, **kw: A.attn_ref_fwd(*a, **kw),
-                                 bwd=lambda *a, **kw: A.attn_ref_bwd(*a, **kw))
+                                 bwd=lambda *a, **kw: A.attn_ref_bwd(*a, **kw),
+                                 decode=lambda *a, **kw: A.attn_ref_decode(*a, **kw))
 
 
 def _rng(seed):
@@ -511,10 +512,65 @@ def pin_gqa_padding(impl):
 
 GQA_PINS = [pin_gqa_torch_sdpa, pin_gqa_finite_difference, pin_gqa_padding]
 
+
+# ------------------------------------------------------------------ decode
+# impl.decode(q, k, v, scale, causal, kv_lens) -> (O, LSE), q [B,H,Nq,d].
+
+def pin_decode_is_last_forward_rows(impl):
+    """Decoding the last Nq positions gives exactly the last Nq rows of the
+    full forward over the same sequence (causal or not, padded or not)."""
+    r = _rng(80)
+    B, H, H_kv, n, d, nq = 2, 4, 2, 12, 3, 3
+    q = r.standard_normal((B, H, n, d))
+    k, v = r.standard_normal((B, H_kv, n, d)), r.standard_normal((B, H_kv, n, d))
+    for causal in (False, True):
+        for sl in (None, np.array([7, 12])):
+            fo, fl = impl.fwd(q, k, v, 0.9, causal, sl)
+            lens = [n, n] if sl is None else sl.tolist()
+            qd = np.stack([q[b, :, L - nq:L] for b, L in enumerate(lens)])
+            do_, dl = impl.decode(qd, k, v, 0.9, causal, sl)
+            for b, L in enumerate(lens):
+                _close(do_[b], fo[b, :, L - nq:L], 1e-13, f"decode O (causal={causal}, L={L})")
+                _close(dl[b], fl[b, :, L - nq:L], 1e-13, f"decode LSE (causal={causal}, L={L})")
+
+
+def pin_decode_torch_lower_right(impl):
+    """Library special case: torch's fp64 SDPA with the lower-right causal bias
+    (the last Nq query positions against Nk keys) and with no mask."""
+    from torch.nn.attention.bias import causal_lower_right
+    r = _rng(81)
+    B, H, nq, nk, d = 2, 3, 4, 10, 5
+    q = r.standard_normal((B, H, nq, d))
+    k, v = r.standard_normal((B, H, nk, d)), r.standard_normal((B, H, nk, d))
+    for causal in (False, True):
+        o, _ = impl.decode(q, k, v, 0.7, causal)
+        tq, tk, tv = (torch.tensor(x) for x in (q, k, v))
+        mask = causal_lower_right(nq, nk) if causal else None
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.7)
+        _close(o, ref.numpy(), 1e-12, f"decode vs torch (causal={causal})")
+
+
+def pin_decode_no_visible_key(impl):
+    """More queries than valid keys under the causal mask: positions below 0
+    see nothing (O = 0, LSE = -inf); an empty sequence likewise."""
+    r = _rng(82)
+    q = r.standard_normal((2, 1, 4, 3))
+    k, v = r.standard_normal((2, 1, 6, 3)), r.standard_normal((2, 1, 6, 3))
+    o, l = impl.decode(q, k, v, 1.0, True, np.array([2, 0]))
+    assert np.all(o[0, 0, :2] == 0) and np.all(np.isneginf(l[0, 0, :2]))
+    assert np.all(np.isfinite(l[0, 0, 2:]))
+    ref_o, _ = impl.head(q[0, 0, 3:4], k[0, 0, :2], v[0, 0, :2], 1.0)
+    _close(o[0, 0, 3:4], ref_o, 1e-13, "last query sees both keys")
+    assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
+
+
+DECODE_PINS = [pin_decode_is_last_forward_rows, pin_decode_torch_lower_right,
+               pin_decode_no_visible_key]
+
 FWD_PINS = [pin_two_block_example, pin_merge_example, pin_safe_softmax_example,
             pin_hand_case_noncausal, pin_hand_case_causal, pin_hand_case_scaled,
             pin_rows_sum_to_one, pin_shift_invariance, pin_value_shift, pin_permutation,
             pin_zero_query, pin_causal_first_row, pin_single_key, pin_padding,
             pin_identical_queries, pin_large_scores, pin_torch_sdpa, pin_online_merge]
 BWD_PINS = [pin_bwd_finite_difference, pin_bwd_torch_autograd, pin_bwd_invariants]
-ALL_PINS = FWD_PINS + BWD_PINS + GQA_PINS
+ALL_PINS = FWD_PINS + BWD_PINS + GQA_PINS + DECODE_PINS

@@ -1,0 +1,107 @@
+"""GPU parity of the split-KV decode (through the C ABI, attn_decode) against the
+fp64 oracle's decode (the last Nq positions of each sequence; causal masking
+is bottom-right aligned).
+
+Tolerances are the forward's (tests/parity.py): the split kernel computes the
+same products and softmax as the forward kernel and the merge is fp32.
+Pages cited (by title):
+  [SafeSoftmax] "FlashAttention：从 Safe Softmax 到分块计算" (§3.2 merge, §10 split K/V)
+  [OpOpt]       "Attention 算子优化:从物化 N×N 矩阵到 FlashAttention 与 PagedAttention" (§五)
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_24_amd as ea
+import oracle
+from attn_inputs import WORKLOADS, make_inputs, make_workload_inputs
+from tests.parity import LSE_TOL, O_TOL, assert_close, dtype_name
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+# (B, H, H_kv, Nq, Nk, d): one token against a ragged cache; 5 tokens, MHA;
+# 4 tokens x group 4 = 16 columns; MQA with 16 heads x 4 tokens = 64 columns
+# (two column blocks); 16 tokens over 129 keys
+SHAPES = [(2, 8, 2, 1, 300, 128), (1, 4, 4, 5, 700, 64), (3, 32, 8, 4, 1000, 128),
+          (1, 16, 1, 4, 333, 128), (2, 2, 2, 16, 129, 64)]
+
+
+def run_decode(x, scale, causal, kv_lens=None, num_splits=0):
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    kl = kv_lens.to(DEV) if kv_lens is not None else None
+    o, lse = ea.attn_decode(q, k, v, scale=scale, causal=causal, kv_lens=kl, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_decode_small(shape, causal, dtype, splits):
+    B, H, H_kv, Nq, Nk, d = shape
+    x = make_inputs(B, H, Nk, d, dtype, seed=sum(shape) + 7 * causal, H_kv=H_kv, Nq=Nq)
+    o, lse = run_decode(x, 1 / math.sqrt(d), causal, num_splits=splits)
+    ro, rl = oracle.attn_ref_decode(x["q"], x["k"], x["v"], 1 / math.sqrt(d), causal)
+    dn = dtype_name(x["q"])
+    assert_close(o, ro, O_TOL[dn], f"decode{shape} O")
+    assert_close(lse, rl, LSE_TOL[dn], f"decode{shape} LSE")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
+def test_decode_kv_lens(causal):
+    """Per-sequence cache lengths: empty, one key, fewer keys than queries (the
+    earliest queries then see nothing under the causal mask), ragged, full."""
+    B, H, H_kv, Nq, Nk, d = 6, 8, 2, 4, 500, 128
+    x = make_inputs(B, H, Nk, d, torch.bfloat16, seed=61 + causal, H_kv=H_kv, Nq=Nq)
+    lens = torch.tensor([0, 1, 3, 257, 500, 64], dtype=torch.int32)
+    o, lse = run_decode(x, 1 / math.sqrt(d), causal, lens, num_splits=4)
+    ro, rl = oracle.attn_ref_decode(x["q"], x["k"], x["v"], 1 / math.sqrt(d), causal, lens)
+    assert_close(o, ro, O_TOL["bf16"], "decode kv_lens O")
+    assert_close(lse, rl, LSE_TOL["bf16"], "decode kv_lens LSE")
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+def test_decode_matches_forward_rows():
+    """With Nq = Nk the decode is the causal forward; for Nq < Nk its rows are
+    the forward's last Nq rows (same products; agreement within the bf16 O
+    tolerance, the two kernels round differently)."""
+    B, H, N, d = 2, 4, 256, 128
+    x = make_inputs(B, H, N, d, torch.bfloat16, seed=62)
+    o_f, l_f = ea.attn_fwd(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), causal=True)
+    qd = x["q"][:, :, N - 8:].contiguous()
+    o_d, l_d = run_decode({"q": qd, "k": x["k"], "v": x["v"]}, 1 / math.sqrt(d), True)
+    assert_close(o_d, o_f[:, :, N - 8:].cpu().double().numpy(), O_TOL["bf16"], "decode vs fwd O")
+    assert_close(l_d, l_f[:, :, N - 8:].cpu().double().numpy(), LSE_TOL["bf16"], "decode vs fwd LSE")
+
+
+def test_decode_split_invariance():
+    """The split count changes only the rounding of the merge."""
+    x = make_inputs(2, 8, 3000, 128, torch.bfloat16, seed=63, H_kv=2, Nq=2)
+    a = run_decode(x, 0.088, True, num_splits=1)
+    b = run_decode(x, 0.088, True, num_splits=0)
+    c = run_decode(x, 0.088, True, num_splits=40)
+    for other in (b, c):
+        assert float((a[0].float() - other[0].float()).abs().max()) <= 2 * 2 ** -8
+        assert float((a[1] - other[1]).abs().max()) <= 1e-4
+
+
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.Nq is not None])
+def test_decode_workload_sampled(name):
+    """The decode workloads at full size, as the benchmark runs them; the oracle
+    evaluates sampled (batch, head) pairs."""
+    w = WORKLOADS[name]
+    x = make_workload_inputs(w)
+    o, lse = run_decode(x, w.scale, w.causal, x["seqlens"])
+    assert torch.isfinite(o).all()
+    rng = np.random.default_rng(w.seed)
+    heads = sorted({(0, 0), (w.B - 1, w.H - 1)} |
+                   {(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(4)})
+    ro, rl = oracle.attn_ref_decode(x["q"], x["k"], x["v"], w.scale, w.causal, x["seqlens"],
+                                    heads=heads)
+    for b, h in heads:
+        assert_close(o[b, h], ro[b, h], O_TOL["bf16"], f"{name} O ({b},{h})")
+        assert_close(lse[b, h], rl[b, h], LSE_TOL["bf16"], f"{name} LSE ({b},{h})")

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as A
-from tests.oracle_pins import ALL_PINS, BWD_PINS, FWD_PINS, GQA_PINS
+from tests.oracle_pins import ALL_PINS, BWD_PINS, DECODE_PINS, FWD_PINS, GQA_PINS
 
 
 def _run_pins(impl, pins):
@@ -161,7 +161,7 @@ def test_backward_mutant_is_caught(name):
 def test_unmutated_backward_copy_passes():
     """The mutant factory with no mutation passes every pin (the harness is sound)."""
     impl = types.SimpleNamespace(head=A.attn_ref_head, bwd_head=_bwd_factory("none"),
-                                 fwd=A.attn_ref_fwd, bwd=A.attn_ref_bwd)
+                                 fwd=A.attn_ref_fwd, bwd=A.attn_ref_bwd, decode=A.attn_ref_decode)
     assert _run_pins(impl, ALL_PINS) == []
 
 
@@ -195,3 +195,33 @@ def test_gqa_interleaved_grouping_is_caught(monkeypatch):
 def test_gqa_missing_group_sum_is_caught():
     impl = types.SimpleNamespace(head=A.attn_ref_head, fwd=A.attn_ref_fwd, bwd=_gqa_bwd_overwrite)
     assert _run_pins(impl, GQA_PINS), "dropped group sum passed every grouped-head pin"
+
+
+# ---- decode mutants: the decode with the query positions misplaced
+
+def _decode_factory(offset_kind):
+    def decode(q, k, v, scale, causal=False, kv_lens=None, heads=None):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        B, H, Nq, _ = q.shape
+        H_kv, Nk = k.shape[1], k.shape[2]
+        o = np.zeros(q.shape[:3] + (v.shape[-1],))
+        lse = np.zeros(q.shape[:3])
+        for b in range(B):
+            L = Nk if kv_lens is None else int(np.clip(kv_lens[b], 0, Nk))
+            pos = {"top_left": np.arange(Nq), "off_by_one": L - Nq + 1 + np.arange(Nq)}[offset_kind]
+            for h in range(H):
+                g = h // (H // H_kv)
+                s = A.mask(A.scores(q[b, h], k[b, g], scale), pos, causal, L)
+                p, m, l = A.softmax_three_pass(s)
+                o[b, h] = p @ v[b, g]
+                with np.errstate(divide="ignore"):
+                    lse[b, h] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+        return o, lse
+    return decode
+
+
+@pytest.mark.parametrize("kind", ["top_left", "off_by_one"])
+def test_decode_position_mutant_is_caught(kind):
+    impl = types.SimpleNamespace(head=A.attn_ref_head, fwd=A.attn_ref_fwd,
+                                 decode=_decode_factory(kind))
+    assert _run_pins(impl, DECODE_PINS), f"decode mutant {kind} passed every decode pin"
