@@ -201,6 +201,41 @@ def bench_suite(torch, ea, steps, warmup):
         del q, k, v, o, lse
 
 
+DECODE_WORKLOADS = ["decode_bf16_b8_h64_hkv8_nq1_nk8192_d128", "decode_bf16_b8_h64_hkv8_nq8_nk8192_d128"]
+
+
+def bench_decode(torch, ea, name, steps, warmup):
+    """Time one split-KV decode call (split kernel + merge) on a decode
+    workload. Decode is bound by HBM bandwidth ("Attention 算子优化..." §五), so the roofline
+    is bytes: K and V over every valid cached position once, Q read, O and LSE
+    written, divided by the median call time, against 8 TB/s."""
+    from attn_inputs import WORKLOADS, make_workload_inputs
+    w = WORKLOADS[name]
+    x = make_workload_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    kl = x["seqlens"].to(dev) if x["seqlens"] is not None else None
+    lens = x["seqlens"].tolist() if x["seqlens"] is not None else [w.N] * w.B
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = torch.empty(ea.attn_decode_workspace_bytes(w.B, w.H, w.kv_heads, w.Nq, w.N, w.d),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush.fill_(1)
+    per = time_launches(torch, lambda: ea.attn_decode(q, k, v, scale=w.scale, causal=w.causal,
+                                                      kv_lens=kl, out=o, lse=lse, workspace=ws),
+                        stream, warmup, steps)
+    med = per[len(per) // 2]
+    kv_bytes = sum(lens) * w.kv_heads * w.d * 2 * 2
+    io_bytes = w.B * w.H * w.Nq * (w.d * 2 * 2 + 4)
+    gbs = (kv_bytes + io_bytes) / (med * 1e-3) / 1e9
+    return {"workload": name, "ms_median": round(med, 4), "ms_p90": round(per[int(0.9 * (len(per) - 1))], 4),
+            "algorithmic_bytes": kv_bytes + io_bytes, "achieved_GBps": round(gbs, 1),
+            "peak_GBps": PEAK_HBM_GBS, "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "bytes_convention": "K,V over every valid cached position + Q read + O, LSE written"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,9 +246,10 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=10,
                     help="timed backward passes on the causal B=2 H=16 N=8192 d=128 workload "
                          "(reported under \"bwd\"; 0 skips them)")
-    ap.add_argument("--mode", choices=["fwd", "bwd", "copy", "suite"], default="fwd",
+    ap.add_argument("--mode", choices=["fwd", "bwd", "copy", "suite", "decode"], default="fwd",
                     help="fwd: the benchmark; bwd: the backward alone; suite: forward timings "
-                         "of every workload plus a context sweep (one JSON line each); copy: a "
+                         "of every workload plus a context sweep (one JSON line each); decode: "
+                         "the split-KV decode workloads against the HBM roofline; copy: a "
                          "plain device copy of known size, whose FETCH_SIZE/WRITE_SIZE counters "
                          "calibrate the traffic figure")
     args = ap.parse_args()
@@ -232,6 +268,11 @@ def main():
         return
     if args.mode == "suite":
         bench_suite(torch, ea, args.steps, args.warmup)
+        return
+    if args.mode == "decode":
+        for name in DECODE_WORKLOADS:
+            print(json.dumps({"mode": "decode", **bench_decode(torch, ea, name, args.steps, args.warmup)}),
+                  flush=True)
         return
     from attn_inputs import WORKLOADS, make_workload_inputs
 
@@ -294,6 +335,7 @@ def main():
     }
     if args.bwd_steps > 0:
         out["bwd"] = bench_backward(torch, ea, args.bwd_steps)
+        out["decode"] = bench_decode(torch, ea, DECODE_WORKLOADS[0], 20, 5)
     if args.cpu_budget > 0:
         out["cpu_baseline"] = cpu_baseline(x, w, args.cpu_budget)
     print(json.dumps(out), flush=True)

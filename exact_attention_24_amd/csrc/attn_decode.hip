@@ -18,8 +18,9 @@
 // share a K/V head ([OpOpt] §五) and their N_q queries are packed into the 32
 // columns of one MFMA block (column c = g*N_q + i), so each K/V byte is read
 // from HBM once for all of them. K/V chunks of 32 keys stream through a
-// per-wave double buffer in LDS by direct buffer->LDS loads; S^T = K Q^T and
-// O^T += V^T P^T run on v_mfma_f32_32x32x16 exactly as in the forward kernel.
+// per-wave three-stage ring in LDS by direct buffer->LDS loads, two chunks in
+// flight ahead of the one being computed; S^T = K Q^T and O^T += V^T P^T run
+// on v_mfma_f32_32x32x16 exactly as in the forward kernel.
 //
 // Query positions: the N_q queries of sequence b are its last N_q positions,
 // L_b - N_q .. L_b - 1, so with causal masking query i sees keys
@@ -41,7 +42,9 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   constexpr int BN = 32;  // keys per chunk
   constexpr int TILE = BN * D * 2;
   constexpr int DS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(1024))) char k0_[TILE], v0_[TILE], k1_[TILE], v1_[TILE];
+  constexpr int LPC = 2 * TileDma<D, BN, 1>::ITER;  // loads per chunk (K and V)
+  __shared__ __attribute__((aligned(1024))) char k0_[TILE], v0_[TILE], k1_[TILE], v1_[TILE],
+      k2_[TILE], v2_[TILE];
 
   const int lane = threadIdx.x, l32 = lane & 31, hi = lane >> 5;
   const int G = a.H / a.H_kv;
@@ -66,19 +69,25 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   const int j_end = min(j_begin + a.chunk_keys, L);
   const int nch = j_end > j_begin ? (j_end - j_begin + BN - 1) / BN : 0;
 
-  const size_t kvoff = (size_t)bkv * a.Nk * D;
-  const TileDma<D, BN, 1> kdma((const e16_t*)a.k + kvoff, j_end, 0, lane);
-  const TileDma<D, BN, 1> vdma((const e16_t*)a.v + kvoff, j_end, 0, lane);
-  if (nch > 0) {
-    kdma.load(lds_base(k0_), j_begin);
-    vdma.load(lds_base(v0_), j_begin);
-  }
-
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   e16x8 qr[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds)
     qr[ds] = as_e16x8(cvalid ? gload16((const e16_t*)a.q + qrow * D + ds * 16 + hi * 8) : zero4);
+
+  const size_t kvoff = (size_t)bkv * a.Nk * D;
+  const TileDma<D, BN, 1> kdma((const e16_t*)a.k + kvoff, j_end, 0, lane);
+  const TileDma<D, BN, 1> vdma((const e16_t*)a.v + kvoff, j_end, 0, lane);
+  auto kst = [&](int st) { return lds_base(st == 0 ? k0_ : st == 1 ? k1_ : k2_); };
+  auto vst = [&](int st) { return lds_base(st == 0 ? v0_ : st == 1 ? v1_ : v2_); };
+  if (nch > 0) {
+    kdma.load(kst(0), j_begin);
+    vdma.load(vst(0), j_begin);
+  }
+  if (nch > 1) {
+    kdma.load(kst(1), j_begin + BN);
+    vdma.load(vst(1), j_begin + BN);
+  }
 
   f32x16 o[DB];
 #pragma unroll
@@ -92,12 +101,19 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
 
   auto chunk = [&](int t, const int st) {
     const int j0 = j_begin + t * BN;
-    if (t + 1 < nch) {
-      kdma.load(lds_base(st ? k0_ : k1_), j0 + BN);
-      vdma.load(lds_base(st ? v0_ : v1_), j0 + BN);
+    // Chunk t+2 goes into the stage chunk t-1 used; then wait for chunk t (the
+    // loads of a wave complete in issue order, so "all but the newest n").
+    if (t + 2 < nch) {
+      kdma.load(kst((st + 2) % 3), j0 + 2 * BN);
+      vdma.load(vst((st + 2) % 3), j0 + 2 * BN);
+      dma_wait_allbut<2 * LPC>();
+    } else if (t + 1 < nch) {
+      dma_wait_allbut<LPC>();
+    } else {
+      dma_wait();
     }
-    const lds_t* Kt = lds_base(st ? k1_ : k0_);
-    const lds_t* Vt = lds_base(st ? v1_ : v0_);
+    const lds_t* Kt = kst(st);
+    const lds_t* Vt = vst(st);
     f32x16 sc = mfma32x32x16_z<F16>(row_operand<D>(Kt, 0, 0, lane), qr[0]);
 #pragma unroll
     for (int ds = 1; ds < DS; ++ds) sc = mfma32x32x16<F16>(row_operand<D>(Kt, 0, ds * 2, lane), qr[ds], sc);
@@ -135,11 +151,11 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
       o[db] = mfma32x32x16<F16>(tr_operand<D>(Vt, 0, db * 32, lane), p0, o[db]);
       o[db] = mfma32x32x16<F16>(tr_operand<D>(Vt, 16, db * 32, lane), p1, o[db]);
     }
-    dma_wait();  // one wave: its own loads landing is all the next chunk needs
   };
-  for (int t = 0; t < nch; t += 2) {
+  for (int t = 0; t < nch; t += 3) {
     chunk(t, 0);
     if (t + 1 < nch) chunk(t + 1, 1);
+    if (t + 2 < nch) chunk(t + 2, 2);
   }
 
   // Partial state of this split: m in log2 units (m_ref * scale * log2 e), the
@@ -178,20 +194,19 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
   const size_t row = blockIdx.x;
   const int t = threadIdx.x;
   const float* ml = a.part_ml + row * a.splits * 2;
+  const float* po = a.part_o + row * a.splits * D + t;
+  // The loads of different splits are independent: unrolled, they are in
+  // flight together instead of one round trip per split.
   float M = -INFINITY;
-  for (int s = 0; s < a.splits; ++s)
-    if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
+#pragma unroll 8
+  for (int s = 0; s < a.splits; ++s) M = ml[2 * s + 1] > 0.f ? fmaxf(M, ml[2 * s]) : M;
   float l = 0.f, acc = 0.f;
-  if (M > -INFINITY) {
-    const float* po = a.part_o + row * a.splits * D + t;
-    for (int s = 0; s < a.splits; ++s) {
-      const float ls = ml[2 * s + 1];
-      if (ls > 0.f) {
-        const float w = fast_exp2(ml[2 * s] - M);
-        l += w * ls;
-        acc += w * po[(size_t)s * D];
-      }
-    }
+#pragma unroll 8
+  for (int s = 0; s < a.splits; ++s) {
+    const float ls = ml[2 * s + 1];
+    const float w = ls > 0.f ? fast_exp2(ml[2 * s] - M) : 0.f;
+    l += w * ls;
+    acc += w * po[(size_t)s * D];
   }
   const bool valid = l > 0.f;
   const float out = valid ? acc / l : 0.f;
