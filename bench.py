@@ -330,7 +330,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic(),
-                     "kernel": "fwd_bf16_kernel<128, causal>",
+                     "kernel": "fwd_16_kernel<128, causal, bf16>",
                      "algorithmic": "4*B*H*N^2*d/2 FLOP per launch"},
     }
     if args.bwd_steps > 0:
