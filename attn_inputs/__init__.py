@@ -23,7 +23,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "draw_seqlens", "workload"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "draw_seqlens", "workload", "fp8_cache"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -51,6 +51,7 @@ class Workload:
     description: str = ""
     H_kv: Optional[int] = None
     Nq: Optional[int] = None
+    kv_fp8: bool = False  # K/V stored as an FP8 cache (see fp8_cache)
 
     @property
     def kv_heads(self) -> int:
@@ -93,6 +94,10 @@ WORKLOADS = {
                  H_kv=8, Nq=8, seqlen_range=(4096, 8192),
                  description="decode of 8 new tokens per sequence (causal among themselves) "
                              "over 4096..8192 cached positions, 64 query heads over 8 K/V heads"),
+        Workload("decode_fp8kv_bf16_b8_h64_hkv8_nq1_nk8192_d128", 8, 64, 8192, 128, "bf16", True,
+                 1010, H_kv=8, Nq=1, kv_fp8=True,
+                 description="decode of one new token over an FP8 (E4M3, per-token scale) K/V "
+                             "cache of 8192 positions, 64 query heads over 8 K/V heads"),
         Workload("gqa_causal_bf16_b2_h32_hkv8_n4096_d128", 2, 32, 4096, 128, "bf16", True, 1006,
                  with_grad=True, H_kv=8,
                  description="grouped-query attention, 32 query heads over 8 K/V heads (the "
@@ -138,6 +143,19 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: torch.dtype = torch.bfloa
     out["seqlens"] = (draw_seqlens(gen, B, *seqlen_range)
                       if seqlen_range is not None else None)
     return out
+
+
+def fp8_cache(x: torch.Tensor):
+    """Store a K or V tensor [..., Nk, d] as an FP8 cache: one fp32 scale per
+    token (row), amax / 448 (448 is E4M3's largest finite value), and the row
+    divided by it rounded to E4M3 by torch's conversion. Returns (uint8 bytes,
+    fp32 scales [..., Nk]). Rows of zeros get scale 1. This builds the inputs
+    that both the HIP path and the oracle read; neither recomputes it."""
+    xf = x.float()
+    amax = xf.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q8 = (xf / scale[..., None]).to(torch.float8_e4m3fn)
+    return q8.view(torch.uint8).contiguous(), scale.contiguous()
 
 
 def make_workload_inputs(w: Workload) -> dict:

@@ -201,7 +201,8 @@ def bench_suite(torch, ea, steps, warmup):
         del q, k, v, o, lse
 
 
-DECODE_WORKLOADS = ["decode_bf16_b8_h64_hkv8_nq1_nk8192_d128", "decode_bf16_b8_h64_hkv8_nq8_nk8192_d128"]
+DECODE_WORKLOADS = ["decode_bf16_b8_h64_hkv8_nq1_nk8192_d128", "decode_bf16_b8_h64_hkv8_nq8_nk8192_d128",
+                    "decode_fp8kv_bf16_b8_h64_hkv8_nq1_nk8192_d128"]
 
 
 def bench_decode(torch, ea, name, steps, warmup):
@@ -209,11 +210,14 @@ def bench_decode(torch, ea, name, steps, warmup):
     workload. Decode is bound by HBM bandwidth ("Attention 算子优化..." §五), so the roofline
     is bytes: K and V over every valid cached position once, Q read, O and LSE
     written, divided by the median call time, against 8 TB/s."""
-    from attn_inputs import WORKLOADS, make_workload_inputs
+    from attn_inputs import WORKLOADS, fp8_cache, make_workload_inputs
     w = WORKLOADS[name]
     x = make_workload_inputs(w)
     dev = torch.device("cuda:0")
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    if w.kv_fp8:  # FP8 (E4M3) cache with per-token scales, built once before timing
+        k8, ks = (t.to(dev) for t in fp8_cache(x["k"]))
+        v8, vs = (t.to(dev) for t in fp8_cache(x["v"]))
     kl = x["seqlens"].to(dev) if x["seqlens"] is not None else None
     lens = x["seqlens"].tolist() if x["seqlens"] is not None else [w.N] * w.B
     o = torch.empty_like(q)
@@ -223,16 +227,22 @@ def bench_decode(torch, ea, name, steps, warmup):
     stream = torch.cuda.current_stream(dev)
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     flush.fill_(1)
-    per = time_launches(torch, lambda: ea.attn_decode(q, k, v, scale=w.scale, causal=w.causal,
-                                                      kv_lens=kl, out=o, lse=lse, workspace=ws),
-                        stream, warmup, steps)
+    if w.kv_fp8:
+        fn = lambda: ea.attn_decode_fp8kv(q, k8, v8, ks, vs, scale=w.scale, causal=w.causal,
+                                          kv_lens=kl, out=o, lse=lse, workspace=ws)
+    else:
+        fn = lambda: ea.attn_decode(q, k, v, scale=w.scale, causal=w.causal, kv_lens=kl, out=o,
+                                    lse=lse, workspace=ws)
+    per = time_launches(torch, fn, stream, warmup, steps)
     med = per[len(per) // 2]
-    kv_bytes = sum(lens) * w.kv_heads * w.d * 2 * 2
+    # K and V: 2 bytes per element, or 1 byte plus a 4-byte scale per token
+    kv_bytes = sum(lens) * w.kv_heads * 2 * ((w.d + 4) if w.kv_fp8 else w.d * 2)
     io_bytes = w.B * w.H * w.Nq * (w.d * 2 * 2 + 4)
     gbs = (kv_bytes + io_bytes) / (med * 1e-3) / 1e9
     return {"workload": name, "ms_median": round(med, 4), "ms_p90": round(per[int(0.9 * (len(per) - 1))], 4),
             "algorithmic_bytes": kv_bytes + io_bytes, "achieved_GBps": round(gbs, 1),
             "peak_GBps": PEAK_HBM_GBS, "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "kv_format": "fp8 e4m3 + per-token fp32 scale" if w.kv_fp8 else w.dtype,
             "bytes_convention": "K,V over every valid cached position + Q read + O, LSE written"}
 
 

@@ -15,7 +15,7 @@ import os
 import pathlib
 from typing import Optional
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode",
+__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_fp8kv",
            "attn_decode_workspace_bytes", "attn_status_string",
            "AttnError", "lib", "LIB_PATH", "DTYPE_F32", "DTYPE_BF16", "DTYPE_F16",
            "EXPORTED_SYMBOLS"]
@@ -28,8 +28,8 @@ DTYPE_BF16 = 1
 DTYPE_F16 = 2
 # Every function include/attn.h declares.
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_gqa", "attn_bwd", "attn_bwd_gqa",
-                    "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes",
-                    "attn_status_string", "attn_last_error")
+                    "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_fp8kv",
+                    "attn_decode_workspace_bytes", "attn_status_string", "attn_last_error")
 
 _lib = None
 
@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
                               i32, vp, sz, vp]
     L.attn_decode.restype = i32
+    L.attn_decode_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    f32, i32, vp, i32, vp, sz, vp]
+    L.attn_decode_fp8kv.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
@@ -261,4 +264,43 @@ def attn_decode(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
                            _seqlens_ptr(kv_lens, B, dev), int(num_splits), workspace.data_ptr(),
                            nbytes, _stream_handle(dev))
     _check(st, "attn_decode")
+    return out, lse
+
+
+def attn_decode_fp8kv(q, k8, v8, k_scale, v_scale, *, scale: Optional[float] = None,
+                      causal: bool = False, kv_lens=None, num_splits: int = 0, out=None, lse=None,
+                      workspace=None):
+    """Split-KV decode over an FP8 (E4M3) K/V cache with per-token fp32 scales:
+    K = k8 * k_scale[..., None], V = v8 * v_scale[..., None]. k8, v8 are
+    [B, H_kv, Nk, d] tensors of torch.float8_e4m3fn or uint8 (the same bytes);
+    k_scale, v_scale are fp32 [B, H_kv, Nk]. Returns (O, LSE) like attn_decode."""
+    import torch
+    B, H, Nq, d = q.shape
+    dev = q.device
+    H_kv = _kv_heads(q, k8)
+    Nk = k8.shape[2]
+    _check_tensor("q", q, (B, H, Nq, d), q.dtype, dev)
+    for name, t in (("k8", k8), ("v8", v8)):
+        if t.dtype not in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+            raise TypeError(f"{name} must be float8_e4m3fn or uint8, not {t.dtype}")
+        _check_tensor(name, t, (B, H_kv, Nk, d), t.dtype, dev)
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _check_tensor(name, t, (B, H_kv, Nk), torch.float32, dev)
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    _check_tensor("out", out, (B, H, Nq, d), q.dtype, dev)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev) if lse is None else lse
+    _check_tensor("lse", lse, (B, H, Nq), torch.float32, dev)
+    need = attn_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d, code, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_fp8kv(q.data_ptr(), k8.data_ptr(), v8.data_ptr(), k_scale.data_ptr(),
+                                 v_scale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, H_kv, Nq,
+                                 Nk, d, code, float(scale), int(bool(causal)),
+                                 _seqlens_ptr(kv_lens, B, dev), int(num_splits), workspace.data_ptr(),
+                                 nbytes, _stream_handle(dev))
+    _check(st, "attn_decode_fp8kv")
     return out, lse

@@ -199,10 +199,13 @@ size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d
   return decode_part_o_bytes(B, H, Nq, d, p.splits) + ml;
 }
 
-attn_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                        int H, int H_kv, int Nq, int Nk, int d, attn_dtype dtype, float scale,
-                        int causal, const int32_t* kv_lens, int num_splits, void* workspace,
-                        size_t workspace_bytes, attn_stream_t stream) {
+namespace {
+
+attn_status decode_common(const void* q, const void* k, const void* v, const float* k_scale,
+                          const float* v_scale, void* o, float* lse, int B, int H, int H_kv,
+                          int Nq, int Nk, int d, attn_dtype dtype, float scale, int causal,
+                          const int32_t* kv_lens, int num_splits, void* workspace,
+                          size_t workspace_bytes, attn_stream_t stream) {
   attn_status st = check_decode(B, H, H_kv, Nq, Nk, d, dtype, num_splits);
   if (st != ATTN_OK) return st;
   if (!q || !k || !v || !o || !workspace) return ATTN_ERR_INVALID_ARG;
@@ -216,6 +219,7 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
   const DecodePlan p = decode_plan(B, H, H_kv, Nq, Nk, num_splits);
   attn::DecArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.kv_lens = kv_lens;
+  a.k_scale = k_scale; a.v_scale = v_scale;
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + decode_part_o_bytes(B, H, Nq, d, p.splits));
   a.B = B; a.H = H; a.H_kv = H_kv; a.Nq = Nq; a.Nk = Nk;
@@ -229,6 +233,30 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
     return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+}  // namespace
+
+attn_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int H_kv, int Nq, int Nk, int d, attn_dtype dtype, float scale,
+                        int causal, const int32_t* kv_lens, int num_splits, void* workspace,
+                        size_t workspace_bytes, attn_stream_t stream) {
+  return decode_common(q, k, v, nullptr, nullptr, o, lse, B, H, H_kv, Nq, Nk, d, dtype, scale,
+                       causal, kv_lens, num_splits, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_fp8kv(const void* q, const uint8_t* k8, const uint8_t* v8,
+                              const float* k_scale, const float* v_scale, void* o, float* lse,
+                              int B, int H, int H_kv, int Nq, int Nk, int d, attn_dtype dtype,
+                              float scale, int causal, const int32_t* kv_lens, int num_splits,
+                              void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  attn_status st = check_decode(B, H, H_kv, Nq, Nk, d, dtype, num_splits);
+  if (st != ATTN_OK) return st;
+  if (d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return ATTN_ERR_INVALID_ARG;
+  return decode_common(q, k8, v8, k_scale, v_scale, o, lse, B, H, H_kv, Nq, Nk, d, dtype, scale,
+                       causal, kv_lens, num_splits, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -22,6 +22,15 @@
 // flight ahead of the one being computed; S^T = K Q^T and O^T += V^T P^T run
 // on v_mfma_f32_32x32x16 exactly as in the forward kernel.
 //
+// FP8 K/V cache ([OpOpt] §六): K and V stored as OCP E4M3 bytes with one fp32
+// scale per token (K_j = k8_j * ks_j, V_j = v8_j * vs_j). HBM carries the
+// 8-bit form; each chunk is widened to the 16-bit format of Q in LDS (every
+// E4M3 value is exact in bf16 and in fp16) and the products run on the
+// matching MFMA. The scales are applied in fp32:
+// ks_j to the scores after the K product (S_ij = ks_j * (q_i . k8_j)), vs_j
+// to the weights before they are rounded for the V product (the row sums use
+// the unscaled weights), so the softmax and accumulation stay fp32.
+//
 // Query positions: the N_q queries of sequence b are its last N_q positions,
 // L_b - N_q .. L_b - 1, so with causal masking query i sees keys
 // j <= L_b - N_q + i (when N_q = L_b this is the forward's top-left mask).
@@ -37,14 +46,57 @@ namespace {
 
 constexpr float kLazyRescaleDec = 8.0f;  // log2 of the largest unnormalised weight
 
-template <int D, bool F16>
+// Two E4M3 bytes (the low or high half of w) widened exactly to the 16-bit
+// format (every E4M3 value is representable in bf16 and in fp16). The scale
+// operand is 1.0: these conversions use only the exponent of their scale.
+template <bool F16>
+__device__ __forceinline__ uint32_t widen2(uint32_t w, bool high) {
+  if constexpr (F16)
+    return __builtin_bit_cast(uint32_t, high ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, true)
+                                             : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, false));
+  else
+    return __builtin_bit_cast(uint32_t, high ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true)
+                                             : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false));
+}
+
+// Widen one chunk of FP8 rows (BN rows of D bytes, laid out by TileDma<D/2>:
+// 16-byte chunk c of row r at c ^ swz<D/2>(r)) into a 16-bit tile in the
+// forward's swizzled layout. Lane l converts half l&1 of row l>>1.
+template <int D, int BN, bool F16>
+__device__ __forceinline__ void widen_fp8_tile(lds_t* dst, const lds_t* src, int lane) {
+  static_assert(BN * 2 == 64, "one lane per half row");
+  const int r = lane >> 1, half = lane & 1;
+  constexpr int C8 = D / 16;  // 16-byte chunks per fp8 row
+#pragma unroll
+  for (int i = 0; i < C8 / 2; ++i) {
+    const int c8 = half * (C8 / 2) + i;
+    const u32x4 w = lds_load16(src + r * D + ((c8 ^ swz<D / 2>(r)) << 4));
+    u32x4 lo, hi;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      lo[2 * j + 0] = widen2<F16>(w[j], false);
+      lo[2 * j + 1] = widen2<F16>(w[j], true);
+      hi[2 * j + 0] = widen2<F16>(w[2 + j], false);
+      hi[2 * j + 1] = widen2<F16>(w[2 + j], true);
+    }
+    lds_store16(dst + tile_off<D>(r, 2 * c8), lo);
+    lds_store16(dst + tile_off<D>(r, 2 * c8 + 1), hi);
+  }
+}
+
+template <int D, bool F16, bool KV8>
 __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   constexpr int BN = 32;  // keys per chunk
-  constexpr int TILE = BN * D * 2;
+  constexpr int DD = KV8 ? D / 2 : D;  // row width in 16-bit units as stored in HBM
+  constexpr int TILE = BN * DD * 2;    // bytes of one stored chunk
   constexpr int DS = D / 16, DB = D / 32;
-  constexpr int LPC = 2 * TileDma<D, BN, 1>::ITER;  // loads per chunk (K and V)
+  constexpr int LPC = 2 * TileDma<DD, BN, 1>::ITER + (KV8 ? 2 : 0);  // loads per chunk
   __shared__ __attribute__((aligned(1024))) char k0_[TILE], v0_[TILE], k1_[TILE], v1_[TILE],
       k2_[TILE], v2_[TILE];
+  // FP8 only: per-stage token scales (64 floats fetched, the first 32 used)
+  // and the bf16 tiles the chunk is widened into.
+  __shared__ __attribute__((aligned(256))) float ks_[KV8 ? 3 : 1][64], vs_[KV8 ? 3 : 1][64];
+  __shared__ __attribute__((aligned(1024))) char kb_[KV8 ? BN * D * 2 : 16], vb_[KV8 ? BN * D * 2 : 16];
 
   const int lane = threadIdx.x, l32 = lane & 31, hi = lane >> 5;
   const int G = a.H / a.H_kv;
@@ -75,19 +127,23 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   for (int ds = 0; ds < DS; ++ds)
     qr[ds] = as_e16x8(cvalid ? gload16((const e16_t*)a.q + qrow * D + ds * 16 + hi * 8) : zero4);
 
-  const size_t kvoff = (size_t)bkv * a.Nk * D;
-  const TileDma<D, BN, 1> kdma((const e16_t*)a.k + kvoff, j_end, 0, lane);
-  const TileDma<D, BN, 1> vdma((const e16_t*)a.v + kvoff, j_end, 0, lane);
+  const size_t kvoff = (size_t)bkv * a.Nk * DD;  // in 16-bit units
+  const TileDma<DD, BN, 1> kdma((const e16_t*)a.k + kvoff, j_end, 0, lane);
+  const TileDma<DD, BN, 1> vdma((const e16_t*)a.v + kvoff, j_end, 0, lane);
   auto kst = [&](int st) { return lds_base(st == 0 ? k0_ : st == 1 ? k1_ : k2_); };
   auto vst = [&](int st) { return lds_base(st == 0 ? v0_ : st == 1 ? v1_ : v2_); };
-  if (nch > 0) {
-    kdma.load(kst(0), j_begin);
-    vdma.load(vst(0), j_begin);
-  }
-  if (nch > 1) {
-    kdma.load(kst(1), j_begin + BN);
-    vdma.load(vst(1), j_begin + BN);
-  }
+  const float* ksh = KV8 ? a.k_scale + (size_t)bkv * a.Nk : nullptr;
+  const float* vsh = KV8 ? a.v_scale + (size_t)bkv * a.Nk : nullptr;
+  auto load_chunk = [&](int st, int j0) {
+    kdma.load(kst(st), j0);
+    vdma.load(vst(st), j0);
+    if constexpr (KV8) {
+      vec64_dma(lds_base((char*)ks_[st]), ksh, j_end, j0, lane);
+      vec64_dma(lds_base((char*)vs_[st]), vsh, j_end, j0, lane);
+    }
+  };
+  if (nch > 0) load_chunk(0, j_begin);
+  if (nch > 1) load_chunk(1, j_begin + BN);
 
   f32x16 o[DB];
 #pragma unroll
@@ -104,8 +160,7 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
     // Chunk t+2 goes into the stage chunk t-1 used; then wait for chunk t (the
     // loads of a wave complete in issue order, so "all but the newest n").
     if (t + 2 < nch) {
-      kdma.load(kst((st + 2) % 3), j0 + 2 * BN);
-      vdma.load(vst((st + 2) % 3), j0 + 2 * BN);
+      load_chunk((st + 2) % 3, j0 + 2 * BN);
       dma_wait_allbut<2 * LPC>();
     } else if (t + 1 < nch) {
       dma_wait_allbut<LPC>();
@@ -114,9 +169,25 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
     }
     const lds_t* Kt = kst(st);
     const lds_t* Vt = vst(st);
+    f32x4 ksc[4], vsc[4];  // FP8: token scales of this lane's 16 keys
+    if constexpr (KV8) {
+      widen_fp8_tile<D, BN, F16>(lds_base(kb_), Kt, lane);
+      widen_fp8_tile<D, BN, F16>(lds_base(vb_), Vt, lane);
+      Kt = lds_base(kb_);
+      Vt = lds_base(vb_);
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        ksc[gq] = *(const f32x4*)&ks_[st][gq * 8 + hi * 4];
+        vsc[gq] = *(const f32x4*)&vs_[st][gq * 8 + hi * 4];
+      }
+    }
     f32x16 sc = mfma32x32x16_z<F16>(row_operand<D>(Kt, 0, 0, lane), qr[0]);
 #pragma unroll
     for (int ds = 1; ds < DS; ++ds) sc = mfma32x32x16<F16>(row_operand<D>(Kt, 0, ds * 2, lane), qr[ds], sc);
+    if constexpr (KV8) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] *= ksc[i >> 2][i & 3];
+    }
     // Element i is key j0 + hi*4 + c (c = (i/4)*8 + i%4); visible iff c <= lim.
     const int lim = last - j0 - hi * 4;
     if (__builtin_amdgcn_ballot_w64(lim < BN - 1)) {
@@ -145,6 +216,10 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
       sum += sc[i];
     }
     l_part += sum;
+    if constexpr (KV8) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] *= vsc[i >> 2][i & 3];
+    }
     const e16x8 p0 = pack8<F16>(sc, 0), p1 = pack8<F16>(sc, 1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -181,9 +256,9 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
 
 // Thin __global__ wrapper (the host pass drops launch stubs of __global__
 // templates whose body holds the buffer-load builtins directly).
-template <int D, bool F16>
+template <int D, bool F16, bool KV8>
 __global__ void __launch_bounds__(64) decode_split_kernel(DecArgs a) {
-  decode_split_body<D, F16>(a);
+  decode_split_body<D, F16, KV8>(a);
 }
 
 // Merge the splits of one query row ([SafeSoftmax] §3.2): with M = max_s m_s,
@@ -215,10 +290,10 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
   if (t == 0 && a.lse) a.lse[row] = valid ? (M + log2f(l)) * kLn2 : -INFINITY;
 }
 
-template <int D, bool F16>
+template <int D, bool F16, bool KV8>
 hipError_t launch_decode_t(const DecArgs& a, hipStream_t stream) {
   const unsigned wgs = (unsigned)(a.B * a.H_kv * a.col_groups * a.splits);
-  hipLaunchKernelGGL((decode_split_kernel<D, F16>), dim3(wgs), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, F16, KV8>), dim3(wgs), dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D, F16>), dim3((unsigned)(a.B * a.H * a.Nq)), dim3(D), 0,
@@ -229,8 +304,12 @@ hipError_t launch_decode_t(const DecArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_16(const DecArgs& a, int d, bool f16, hipStream_t stream) {
-  if (d == 64) return f16 ? launch_decode_t<64, true>(a, stream) : launch_decode_t<64, false>(a, stream);
-  return f16 ? launch_decode_t<128, true>(a, stream) : launch_decode_t<128, false>(a, stream);
+  if (a.k_scale) {  // FP8 K/V (d = 128 only; checked by the caller)
+    return f16 ? launch_decode_t<128, true, true>(a, stream) : launch_decode_t<128, false, true>(a, stream);
+  }
+  if (d == 64)
+    return f16 ? launch_decode_t<64, true, false>(a, stream) : launch_decode_t<64, false, false>(a, stream);
+  return f16 ? launch_decode_t<128, true, false>(a, stream) : launch_decode_t<128, false, false>(a, stream);
 }
 
 }  // namespace attn

@@ -49,6 +49,8 @@ struct DecArgs {
   void* o;
   float* lse;               // may be null
   const int32_t* kv_lens;   // may be null (every sequence has Nk keys)
+  const float* k_scale;     // FP8 K/V only: per-token scales [B,H_kv,Nk]; null for 16-bit K/V
+  const float* v_scale;
   float* part_o;            // workspace: [B*H*Nq][splits][D] unnormalised partial O
   float* part_ml;           // workspace: [B*H*Nq][splits][2] = (m * scale * log2 e, l)
   int B, H, H_kv, Nq, Nk;

@@ -28,6 +28,8 @@
  *    token and is bandwidth-bound).
  *  - "FlashAttention：从 Safe Softmax 到分块计算" §10 (splitting the K/V range
  *    across workgroups for decode, partial states combined by the §3.2 merge).
+ *  - "Attention 算子优化..." §六 (FP8 E4M3 K/V cache with per-token scales,
+ *    dequantised on chip; softmax and accumulation in fp32, products in 16-bit).
  *
  * Conventions shared by every entry point
  *  - Tensors are [B, H, N, d], contiguous, d fastest (element (b,h,i,c) sits at
@@ -190,6 +192,25 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
                         int B, int H, int H_kv, int Nq, int Nk, int d, attn_dtype dtype,
                         float scale, int causal, const int32_t* kv_lens, int num_splits,
                         void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
+/*
+ * attn_decode_fp8kv - attn_decode over an FP8 K/V cache.
+ *
+ *  k8, v8    [B,H_kv,Nk,d] bytes, OCP FP8 E4M3 (sign, 4 exponent bits with bias
+ *            7, 3 mantissa bits; 0x7F/0xFF are NaN, no infinities), read only.
+ *  k_scale, v_scale  [B,H_kv,Nk] fp32 per-token scales: the keys and values
+ *            are K_j = k8_j * k_scale_j and V_j = v8_j * v_scale_j.
+ * q, o, lse, dtype (of q and o), kv_lens, causal, num_splits and the workspace
+ * (attn_decode_workspace_bytes with the same arguments) are as for attn_decode.
+ * Only d = 128 is implemented (ATTN_ERR_UNSUPPORTED otherwise). HBM carries
+ * the 8-bit K/V; each chunk is widened to bf16 on chip (exact), the scales are
+ * applied in fp32 to the scores and to the weights before the V product.
+ */
+attn_status attn_decode_fp8kv(const void* q, const uint8_t* k8, const uint8_t* v8,
+                              const float* k_scale, const float* v_scale, void* o, float* lse,
+                              int B, int H, int H_kv, int Nq, int Nk, int d, attn_dtype dtype,
+                              float scale, int causal, const int32_t* kv_lens, int num_splits,
+                              void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* attn_status_string(attn_status s);

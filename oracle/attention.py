@@ -51,6 +51,12 @@ Readings taken where the pages are silent (each is listed in the design notes):
     L_b - Nq .. L_b - 1, so under the causal mask query i sees keys
     j <= L_b - Nq + i (bottom-right alignment; for Nq = L_b it is the
     forward's mask). Without the mask it sees every valid key.
+  * FP8 K/V cache ([OpOpt] §六: K, V stored as FP8 E4M3 with per-token
+    scales, dequantised before use): the oracle decodes each byte by the OCP
+    E4M3 definition (sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+    exponent 0 is subnormal; 0x7F and 0xFF are NaN; no infinities) and
+    multiplies by the token's scale in fp64; attention then runs on those
+    values exactly as above.
   * Backward ([AIInfra] §2.3 gives dV = P^T dO and dS = P o (dP - rowsum(dP o P))
     with dP = dO V^T; the scale factor on dQ and dK is not on the pages and
     follows from S = scale * Q K^T by the chain rule):
@@ -62,7 +68,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["scores", "mask", "softmax_three_pass", "attn_ref_head", "kv_head", "attn_ref_fwd",
-           "attn_ref_rows", "attn_ref_decode", "attn_ref_bwd_head", "attn_ref_bwd"]
+           "attn_ref_rows", "attn_ref_decode", "e4m3_decode", "dequant_fp8",
+           "attn_ref_bwd_head", "attn_ref_bwd"]
 
 
 def _f64(x) -> np.ndarray:
@@ -206,6 +213,25 @@ def attn_ref_decode(q, k, v, scale: float, causal: bool = False, kv_lens=None, h
         with np.errstate(divide="ignore"):
             lse[b, h] = np.where(l > 0.0, m + np.log(np.where(l > 0.0, l, 1.0)), -np.inf)
     return o, lse
+
+
+def e4m3_decode(byte_values) -> np.ndarray:
+    """The value of each FP8 E4M3 byte, by the format's definition."""
+    u = np.asarray(byte_values, dtype=np.int64)
+    sign = np.where(u >> 7, -1.0, 1.0)
+    e = (u >> 3) & 15
+    m = (u & 7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e - 7.0)
+    sub = (m / 8.0) * np.exp2(-6.0)
+    v = sign * np.where(e == 0, sub, normal)
+    return np.where((e == 15) & ((u & 7) == 7), np.nan, v)
+
+
+def dequant_fp8(x8, scale) -> np.ndarray:
+    """FP8 cache [..., N, d] (uint8 bytes) and per-token scales [..., N] ->
+    fp64 values x8 * scale."""
+    b = x8.detach().cpu().numpy() if hasattr(x8, "detach") else np.asarray(x8)
+    return e4m3_decode(b) * _f64(scale)[..., None]
 
 
 def attn_ref_rows(q, k, v, b: int, h: int, rows, scale: float, causal: bool = False,

@@ -39,7 +39,8 @@ def oracle_impl():
                                  bwd_head=lambda *a, **kw: A.attn_ref_bwd_head(*a, **kw),
                                  fwd=lambda *a, **kw: A.attn_ref_fwd(*a, **kw),
                                  bwd=lambda *a, **kw: A.attn_ref_bwd(*a, **kw),
-                                 decode=lambda *a, **kw: A.attn_ref_decode(*a, **kw))
+                                 decode=lambda *a, **kw: A.attn_ref_decode(*a, **kw),
+                                 e4m3=lambda *a, **kw: A.e4m3_decode(*a, **kw))
 
 
 def _rng(seed):
@@ -564,8 +565,24 @@ def pin_decode_no_visible_key(impl):
     assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
 
 
+def pin_e4m3_values(impl):
+    """The E4M3 decoder: hand values of the format (1.0, the largest finite 448,
+    the smallest subnormal 2^-9, -0, NaN) and, for all 256 bytes, torch's own
+    float8_e4m3fn conversion (a library special case)."""
+    f = impl.e4m3
+    assert f([0x38])[0] == 1.0 and f([0x7E])[0] == 448.0 and f([0x01])[0] == 2.0 ** -9
+    assert f([0x08])[0] == 2.0 ** -6 and f([0xC0])[0] == -2.0
+    assert f([0x80])[0] == 0.0 and np.signbit(f([0x80])[0])
+    assert np.isnan(f([0x7F])[0]) and np.isnan(f([0xFF])[0])
+    allb = np.arange(256)
+    ref = torch.tensor(allb, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = f(allb)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert np.all(same), f"E4M3 bytes {allb[~same][:8]} decode differently"
+
+
 DECODE_PINS = [pin_decode_is_last_forward_rows, pin_decode_torch_lower_right,
-               pin_decode_no_visible_key]
+               pin_decode_no_visible_key, pin_e4m3_values]
 
 FWD_PINS = [pin_two_block_example, pin_merge_example, pin_safe_softmax_example,
             pin_hand_case_noncausal, pin_hand_case_causal, pin_hand_case_scaled,

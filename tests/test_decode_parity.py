@@ -16,7 +16,7 @@ import torch
 
 import exact_attention_24_amd as ea
 import oracle
-from attn_inputs import WORKLOADS, make_inputs, make_workload_inputs
+from attn_inputs import WORKLOADS, fp8_cache, make_inputs, make_workload_inputs
 from tests.parity import LSE_TOL, O_TOL, assert_close, dtype_name
 
 pytestmark = pytest.mark.gpu
@@ -89,7 +89,7 @@ def test_decode_split_invariance():
         assert float((a[1] - other[1]).abs().max()) <= 1e-4
 
 
-@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.Nq is not None])
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.Nq is not None and not w.kv_fp8])
 def test_decode_workload_sampled(name):
     """The decode workloads at full size, as the benchmark runs them; the oracle
     evaluates sampled (batch, head) pairs."""
@@ -105,3 +105,73 @@ def test_decode_workload_sampled(name):
     for b, h in heads:
         assert_close(o[b, h], ro[b, h], O_TOL["bf16"], f"{name} O ({b},{h})")
         assert_close(lse[b, h], rl[b, h], LSE_TOL["bf16"], f"{name} LSE ({b},{h})")
+
+
+# ------------------------------------------------------------- FP8 K/V cache
+
+def run_decode_fp8(q, k8, v8, ks, vs, scale, causal, kv_lens=None, num_splits=0):
+    t = [x.to(DEV) for x in (q, k8, v8, ks, vs)]
+    kl = kv_lens.to(DEV) if kv_lens is not None else None
+    o, lse = ea.attn_decode_fp8kv(*t, scale=scale, causal=causal, kv_lens=kl, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def _fp8_case(x):
+    k8, ks = fp8_cache(x["k"])
+    v8, vs = fp8_cache(x["v"])
+    return k8, v8, ks, vs, oracle.dequant_fp8(k8, ks), oracle.dequant_fp8(v8, vs)
+
+
+FP8_SHAPES = [(2, 8, 2, 1, 300), (1, 16, 1, 4, 333), (2, 4, 4, 3, 700), (1, 8, 8, 16, 129)]
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
+@pytest.mark.parametrize("shape", FP8_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_decode_fp8kv_small(shape, causal, dtype, splits):
+    """FP8 (E4M3, per-token scale) K/V: the oracle attends over the dequantised
+    cache in fp64; the bar is the 16-bit path's (the FP8 values are exact on
+    chip, the scales are applied in fp32)."""
+    B, H, H_kv, Nq, Nk = shape
+    x = make_inputs(B, H, Nk, 128, dtype, seed=sum(shape) + 5 * causal, H_kv=H_kv, Nq=Nq)
+    k8, v8, ks, vs, kd, vd = _fp8_case(x)
+    o, lse = run_decode_fp8(x["q"], k8, v8, ks, vs, 1 / math.sqrt(128), causal, num_splits=splits)
+    ro, rl = oracle.attn_ref_decode(x["q"], kd, vd, 1 / math.sqrt(128), causal)
+    dn = dtype_name(x["q"])
+    assert_close(o, ro, O_TOL[dn], f"fp8 decode{shape} O")
+    assert_close(lse, rl, LSE_TOL[dn], f"fp8 decode{shape} LSE")
+
+
+def test_decode_fp8kv_lens_and_scales():
+    """Cache lengths 0..Nk and per-token scales spanning six orders of magnitude
+    (rows scaled by 10^-3 .. 10^3 before quantisation)."""
+    B, H, H_kv, Nq, Nk = 4, 8, 2, 2, 400
+    x = make_inputs(B, H, Nk, 128, torch.bfloat16, seed=71, H_kv=H_kv, Nq=Nq)
+    mag = torch.logspace(-3, 3, Nk)[None, None, :, None]
+    x["k"] = (x["k"].float() * mag).to(torch.bfloat16)
+    x["v"] = (x["v"].float() * mag.flip(2)).to(torch.bfloat16)
+    k8, v8, ks, vs, kd, vd = _fp8_case(x)
+    lens = torch.tensor([0, 1, 250, 400], dtype=torch.int32)
+    q = (x["q"].float() * 1e-3).to(torch.bfloat16)  # keep scores O(1) against |K| up to 10^3
+    o, lse = run_decode_fp8(q, k8, v8, ks, vs, 1 / math.sqrt(128), True, lens, num_splits=5)
+    ro, rl = oracle.attn_ref_decode(q, kd, vd, 1 / math.sqrt(128), True, lens)
+    scale_v = float(np.abs(vd).max())
+    assert_close(o, ro, O_TOL["bf16"] * scale_v, "fp8 decode lens O")
+    assert_close(lse, rl, LSE_TOL["bf16"], "fp8 decode lens LSE")
+
+
+def test_decode_fp8kv_workload_sampled():
+    """The FP8 decode workload at full size (B=8, 64 query heads over 8 K/V
+    heads, 8192 cached positions, one new token), as the benchmark runs it."""
+    w = WORKLOADS["decode_fp8kv_bf16_b8_h64_hkv8_nq1_nk8192_d128"]
+    x = make_workload_inputs(w)
+    k8, v8, ks, vs, kd, vd = _fp8_case(x)
+    o, lse = run_decode_fp8(x["q"], k8, v8, ks, vs, w.scale, w.causal)
+    assert torch.isfinite(o).all()
+    heads = [(0, 0), (3, 17), (7, 63)]
+    ro, rl = oracle.attn_ref_decode(x["q"], kd, vd, w.scale, w.causal, heads=heads)
+    for b, h in heads:
+        assert_close(o[b, h], ro[b, h], O_TOL["bf16"], f"fp8 workload O ({b},{h})")
+        assert_close(lse[b, h], rl[b, h], LSE_TOL["bf16"], f"fp8 workload LSE ({b},{h})")

@@ -161,7 +161,8 @@ def test_backward_mutant_is_caught(name):
 def test_unmutated_backward_copy_passes():
     """The mutant factory with no mutation passes every pin (the harness is sound)."""
     impl = types.SimpleNamespace(head=A.attn_ref_head, bwd_head=_bwd_factory("none"),
-                                 fwd=A.attn_ref_fwd, bwd=A.attn_ref_bwd, decode=A.attn_ref_decode)
+                                 fwd=A.attn_ref_fwd, bwd=A.attn_ref_bwd, decode=A.attn_ref_decode,
+                                 e4m3=A.e4m3_decode)
     assert _run_pins(impl, ALL_PINS) == []
 
 
@@ -223,5 +224,26 @@ def _decode_factory(offset_kind):
 @pytest.mark.parametrize("kind", ["top_left", "off_by_one"])
 def test_decode_position_mutant_is_caught(kind):
     impl = types.SimpleNamespace(head=A.attn_ref_head, fwd=A.attn_ref_fwd,
-                                 decode=_decode_factory(kind))
+                                 decode=_decode_factory(kind), e4m3=A.e4m3_decode)
     assert _run_pins(impl, DECODE_PINS), f"decode mutant {kind} passed every decode pin"
+
+
+def _e4m3_bias8(byte_values):
+    """E4M3 with the exponent bias off by one (8 instead of 7)."""
+    return A.e4m3_decode(byte_values) / 2.0
+
+
+def _e4m3_no_subnormals(byte_values):
+    """E4M3 with exponent field 0 read as a normal number."""
+    u = np.asarray(byte_values, dtype=np.int64)
+    v = A.e4m3_decode(byte_values)
+    e, m = (u >> 3) & 15, (u & 7)
+    fixed = np.where(u >> 7, -1.0, 1.0) * (1.0 + m / 8.0) * np.exp2(-7.0)
+    return np.where(e == 0, fixed, v)
+
+
+@pytest.mark.parametrize("fn", [_e4m3_bias8, _e4m3_no_subnormals], ids=["bias8", "no_subnormals"])
+def test_e4m3_mutant_is_caught(fn):
+    impl = types.SimpleNamespace(head=A.attn_ref_head, fwd=A.attn_ref_fwd, decode=A.attn_ref_decode,
+                                 e4m3=fn)
+    assert _run_pins(impl, DECODE_PINS), "E4M3 decoder mutant passed every pin"
