@@ -44,8 +44,12 @@ attn_status check_heads(int H, int H_kv) {
 }
 
 // Split plan of the decode: `splits` key ranges of `chunk_keys` keys (a
-// multiple of 32) per (batch, K/V head); 0 requested splits picks enough to
-// give about 2048 single-wave workgroups (at least 32 keys per split).
+// multiple of 32) per (batch, K/V head). 0 requested splits picks enough for
+// about 768 single-wave workgroups: one resident round at three per CU (the
+// split kernel's 42-48 KiB of LDS) on 256 CUs. More, shorter workgroups were
+// measured slower (each pays its start-up latency again; B=8, 8 K/V heads,
+// 8192 keys: 32 splits 52.7 us, 12 splits 49.6 us for bf16, 53.7 -> 46.9 us
+// for FP8 K/V).
 struct DecodePlan {
   int splits, chunk_keys, col_groups;
 };
@@ -55,7 +59,7 @@ DecodePlan decode_plan(int B, int H, int H_kv, int Nq, int Nk, int num_splits) {
   long long want = num_splits;
   if (want <= 0) {
     const long long units = (long long)B * H_kv * p.col_groups;
-    want = (2048 + units - 1) / units;
+    want = (768 + units - 1) / units;
   }
   const long long max_splits = (Nk + 31) / 32;
   if (want > max_splits) want = max_splits;
