@@ -151,7 +151,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   // dK, dV sum the contributions of the G = H / H_kv query heads that read
   // this K/V head (query head h reads K/V head h / G).
   int bkv, kt;
-  tile_order(blockIdx.x, nkt, a.B * a.H_kv, false, bkv, kt);
+  tile_order(blockIdx.x, nkt, a.B * a.H_kv, 1, false, bkv, kt);
   const int b = bkv / a.H_kv, G = a.H / a.H_kv;
   const int hq0 = b * a.H + (bkv % a.H_kv) * G;  // first query head of the group
   const int L = seq_len(a, b);
@@ -414,7 +414,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   const int N = a.N;
   const int nm = (N + BM - 1) / BM;
   int bh, mt;
-  tile_order(blockIdx.x, nm, a.B * a.H, CAUSAL, bh, mt);
+  tile_order(blockIdx.x, nm, a.B * a.H, a.H / a.H_kv, CAUSAL, bh, mt);
   const int L = seq_len(a, bh / a.H);
   const int m0 = mt * BM;
   const size_t hoff = (size_t)bh * N * D;

@@ -73,7 +73,7 @@ __device__ __forceinline__ void fwd_16_body(const FwdArgs& a) {
   const int N = a.N;
   const int nm = (N + BM - 1) / BM;
   int bh, mt;
-  tile_order(blockIdx.x, nm, a.B * a.H, CAUSAL, bh, mt);
+  tile_order(blockIdx.x, nm, a.B * a.H, a.H / a.H_kv, CAUSAL, bh, mt);
   const int b = bh / a.H;
   int L = N;
   if (a.seqlens) L = min(max(a.seqlens[b], 0), N);
@@ -370,13 +370,6 @@ hipError_t launch_fwd_16(const FwdArgs& a, int d, bool causal, bool f16, hipStre
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
   if (d == 64) return causal ? launch_f32_t<64, true>(a, stream) : launch_f32_t<64, false>(a, stream);
   return causal ? launch_f32_t<128, true>(a, stream) : launch_f32_t<128, false>(a, stream);
-}
-
-void tile_order_host(int block, int num_tiles, int num_heads, bool heavy_first, int* head, int* tile) {
-  int h, t;
-  tile_order(block, num_tiles, num_heads, heavy_first, h, t);
-  *head = h;
-  *tile = t;
 }
 
 }  // namespace attn

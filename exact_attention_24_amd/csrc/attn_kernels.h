@@ -68,9 +68,4 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stre
 hipError_t launch_bwd_16(const BwdArgs& a, int d, bool causal, bool f16, hipStream_t stream);
 hipError_t launch_decode_16(const DecArgs& a, int d, bool f16, hipStream_t stream);
 
-// Host-side mirror of the workgroup -> (head, row tile) order used by the
-// forward kernels (exposed for tests of the scheduling logic).
-void tile_order_host(int block, int num_tiles, int num_heads, bool heavy_first, int* head,
-                     int* tile);
-
 }  // namespace attn

@@ -8,16 +8,22 @@ namespace attn {
 // heavy_first (causal masks, where the last row tiles visit the most KV
 // tiles) every head's heaviest tile is launched before any lighter one, so
 // the longest workgroups start earliest and the launch ends on short ones.
-// Within one row tile the heads are split over the XCDs: when the head count
-// is a multiple of 8, workgroup b runs on XCD b % 8 and only ever touches
-// heads xcd*H/8 .. xcd*H/8 + H/8 - 1, so each head's K/V is cached in one L2.
-__host__ __device__ inline void tile_order(int block, int num_tiles, int num_heads,
+// Within one row tile the heads are dealt to the XCDs: when the head count is
+// a multiple of 8 groups, workgroup b runs on XCD b % 8 and only ever touches
+// the heads of that XCD, so each head's K/V is cached in one L2. Heads are
+// dealt in units of `group` consecutive heads (the query heads that share one
+// K/V head, which then share that L2 too), and the units are interleaved over
+// the XCDs (unit u on XCD u % 8): every XCD gets heads of every sequence, so a
+// padded batch whose sequences differ in length still loads the XCDs evenly.
+__host__ __device__ inline void tile_order(int block, int num_tiles, int num_heads, int group,
                                            bool heavy_first, int& head, int& tile) {
   int r;
-  if ((num_heads & 7) == 0) {
+  if (group >= 1 && num_heads % group == 0 && ((num_heads / group) & 7) == 0) {
     const int xcd = block & 7, slot = block >> 3;
     const int heads_per_xcd = num_heads >> 3;
-    head = xcd * heads_per_xcd + slot % heads_per_xcd;
+    const int s = slot % heads_per_xcd;        // which of this XCD's heads
+    const int unit = (s / group) * 8 + xcd;    // units u with u % 8 == xcd
+    head = unit * group + s % group;
     r = slot / heads_per_xcd;
   } else {
     head = block % num_heads;
