@@ -102,8 +102,10 @@ __device__ __forceinline__ void fwd_16_body(const FwdArgs& a) {
   const int w_end = (qw >= L) ? 0 : (CAUSAL ? min(L, qw + 32) : L);
   const int wnt = (w_end + BN - 1) / BN;                 // tiles this wave computes
 
-  const TileDma<D, BN, 4> kdma((const e16_t*)a.k + kvoff, N, wave, lane);
-  const TileDma<D, BN, 4> vdma((const e16_t*)a.v + kvoff, N, wave, lane);
+  // K/V rows at or past L are never fetched (the DMA reads zeros there), so
+  // whatever the padding holds cannot reach a valid row through 0 * x.
+  const TileDma<D, BN, 4> kdma((const e16_t*)a.k + kvoff, L, wave, lane);
+  const TileDma<D, BN, 4> vdma((const e16_t*)a.v + kvoff, L, wave, lane);
   kdma.load(kst[0], 0);
   vdma.load(vst[0], 0);
 
@@ -111,7 +113,7 @@ __device__ __forceinline__ void fwd_16_body(const FwdArgs& a) {
   e16x8 qr[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds)
-    qr[ds] = as_e16x8(q < N ? gload16(Qh + (size_t)q * D + ds * 16 + hi * 8) : zero4);
+    qr[ds] = as_e16x8(q < L ? gload16(Qh + (size_t)q * D + ds * 16 + hi * 8) : zero4);
 
   f32x16 o[DB];
 #pragma unroll
@@ -268,7 +270,7 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a) {
   float4 qv[C4], acc[C4];
 #pragma unroll
   for (int c = 0; c < C4; ++c) {
-    qv[c] = q < N ? Qh[(size_t)q * C4 + c] : z;
+    qv[c] = q < L ? Qh[(size_t)q * C4 + c] : z;
     acc[c] = z;
   }
   float m_run = kMaxInit, l_run = 0.f;
@@ -278,8 +280,8 @@ __global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a) {
     __syncthreads();
     for (int e = lane; e < BN * C4; e += 64) {
       const int r = e / C4, c = e % C4, g = n0 + r;
-      ks[r][c] = g < N ? Kh[(size_t)g * C4 + c] : z;
-      vs[r][c] = g < N ? Vh[(size_t)g * C4 + c] : z;
+      ks[r][c] = g < L ? Kh[(size_t)g * C4 + c] : z;
+      vs[r][c] = g < L ? Vh[(size_t)g * C4 + c] : z;
     }
     __syncthreads();
     float s[BN];

@@ -113,6 +113,27 @@ def test_f16_workload_sampled_heads():
         check_grads(tuple(g[b, h] for g in got), ref, f"f16 N=4096 head ({b},{h})")
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
+def test_backward_padding_contents_never_read(causal):
+    """NaN in every padded position of Q, K, V and dO: gradients of valid
+    positions match the oracle's on clean inputs, padded ones are exactly 0."""
+    B, H, N, d = 3, 2, 333, 128
+    x = make_inputs(B, H, N, d, torch.bfloat16, seed=79, with_grad=True)
+    x["seqlens"] = torch.tensor([100, 333, 0], dtype=torch.int32)
+    ref = oracle.attn_ref_bwd(x["q"], x["k"], x["v"], x["do"], 1 / math.sqrt(d), causal,
+                              x["seqlens"])
+    for b, L in enumerate(x["seqlens"].tolist()):
+        for n in ("q", "k", "v", "do"):
+            x[n][b, :, L:] = float("nan")
+    got = run_fwd_bwd(x, 1 / math.sqrt(d), causal)
+    for b, L in enumerate(x["seqlens"].tolist()):
+        for g in got:
+            assert torch.all(g[b, :, L:] == 0), "padded rows/keys must get zero gradient"
+        if L > 1:
+            check_grads(tuple(g[b:b + 1, :, :L] for g in got),
+                        tuple(r[b:b + 1, :, :L] for r in ref), f"NaN padding b={b}")
+
+
 def test_backward_deterministic():
     x = make_inputs(1, 4, 700, 128, torch.bfloat16, seed=31, with_grad=True)
     a = run_fwd_bwd(x, 0.088, True)

@@ -202,6 +202,27 @@ def test_f16_large_values(d):
     assert_close(lse, rl, LSE_TOL["f16"], "f16 large values LSE")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
+def test_padding_contents_never_read(causal, dtype):
+    """Padded positions (at or past a sequence's length) hold NaN in Q, K and V:
+    valid rows must still match the oracle (which never looks at them) and
+    padded rows must be exactly 0 / -inf."""
+    B, H, N, d = 3, 2, 333, 128
+    x = make_inputs(B, H, N, d, dtype, seed=78)
+    x["seqlens"] = torch.tensor([100, 333, 0], dtype=torch.int32)
+    clean = {k_: (v_.clone() if v_ is not None else None) for k_, v_ in x.items()}
+    for b, L in enumerate(x["seqlens"].tolist()):
+        for n in ("q", "k", "v"):
+            x[n][b, :, L:] = float("nan")
+    o, lse = run_fwd(x["q"], x["k"], x["v"], 1 / math.sqrt(d), causal, x["seqlens"])
+    ro, rl = oracle.attn_ref_fwd(clean["q"], clean["k"], clean["v"], 1 / math.sqrt(d), causal,
+                                 clean["seqlens"])
+    dn = dtype_name(x["q"])
+    assert_close(o, ro, O_TOL[dn], "NaN padding O")
+    assert_close(lse, rl, LSE_TOL[dn], "NaN padding LSE")
+
+
 def test_deterministic():
     x = make_inputs(2, 4, 1000, 128, torch.bfloat16, seed=5)
     a = run_fwd(x["q"], x["k"], x["v"], 0.088, True)
