@@ -84,6 +84,18 @@ __device__ __forceinline__ void widen_fp8_tile(lds_t* dst, const lds_t* src, int
   }
 }
 
+// A operand of the score MFMA for k step ds, straight from an FP8 tile in the
+// layout above: lane l takes key row l%32, bytes 16*ds + 8*(l/32) .. +7 (eight
+// consecutive d), widened exactly in registers (no 16-bit copy of K in LDS).
+template <int D, bool F16>
+__device__ __forceinline__ e16x8 fp8_row_operand(const lds_t* tile, int ds, int lane) {
+  const int r = lane & 31;
+  const u32x2 w = lds_load8(tile + r * D + ((ds ^ swz<D / 2>(r)) << 4) + (lane >> 5) * 8);
+  const u32x4 e = {widen2<F16>(w[0], false), widen2<F16>(w[0], true), widen2<F16>(w[1], false),
+                   widen2<F16>(w[1], true)};
+  return as_e16x8(e);
+}
+
 template <int D, bool F16, bool KV8>
 __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   constexpr int BN = 32;  // keys per chunk
@@ -91,12 +103,15 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   constexpr int TILE = BN * DD * 2;    // bytes of one stored chunk
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int LPC = 2 * TileDma<DD, BN, 1>::ITER + (KV8 ? 2 : 0);  // loads per chunk
-  __shared__ __attribute__((aligned(1024))) char k0_[TILE], v0_[TILE], k1_[TILE], v1_[TILE],
-      k2_[TILE], v2_[TILE];
+  // Ring of NST chunk stages, NST - 1 chunks in flight. An FP8 chunk is half
+  // the bytes of a 16-bit one, so its ring is deeper: both keep about 32 KiB
+  // per wave in flight (a split is bound by its loads' latency, not by HBM).
+  constexpr int NST = KV8 ? 5 : 3;
+  __shared__ __attribute__((aligned(1024))) char kr_[NST][TILE], vr_[NST][TILE];
   // FP8 only: per-stage token scales (64 floats fetched, the first 32 used)
-  // and the bf16 tiles the chunk is widened into.
-  __shared__ __attribute__((aligned(256))) float ks_[KV8 ? 3 : 1][64], vs_[KV8 ? 3 : 1][64];
-  __shared__ __attribute__((aligned(1024))) char kb_[KV8 ? BN * D * 2 : 16], vb_[KV8 ? BN * D * 2 : 16];
+  // and the 16-bit tile V is widened into (K is widened in registers).
+  __shared__ __attribute__((aligned(256))) float ks_[KV8 ? NST : 1][64], vs_[KV8 ? NST : 1][64];
+  __shared__ __attribute__((aligned(1024))) char vb_[KV8 ? BN * D * 2 : 16];
 
   const int lane = threadIdx.x, l32 = lane & 31, hi = lane >> 5;
   const int G = a.H / a.H_kv;
@@ -130,8 +145,8 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   const size_t kvoff = (size_t)bkv * a.Nk * DD;  // in 16-bit units
   const TileDma<DD, BN, 1> kdma((const e16_t*)a.k + kvoff, j_end, 0, lane);
   const TileDma<DD, BN, 1> vdma((const e16_t*)a.v + kvoff, j_end, 0, lane);
-  auto kst = [&](int st) { return lds_base(st == 0 ? k0_ : st == 1 ? k1_ : k2_); };
-  auto vst = [&](int st) { return lds_base(st == 0 ? v0_ : st == 1 ? v1_ : v2_); };
+  auto kst = [&](int st) { return lds_base(kr_[st]); };
+  auto vst = [&](int st) { return lds_base(vr_[st]); };
   const float* ksh = KV8 ? a.k_scale + (size_t)bkv * a.Nk : nullptr;
   const float* vsh = KV8 ? a.v_scale + (size_t)bkv * a.Nk : nullptr;
   auto load_chunk = [&](int st, int j0) {
@@ -142,8 +157,9 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
       vec64_dma(lds_base((char*)vs_[st]), vsh, j_end, j0, lane);
     }
   };
-  if (nch > 0) load_chunk(0, j_begin);
-  if (nch > 1) load_chunk(1, j_begin + BN);
+#pragma unroll
+  for (int c = 0; c < NST - 1; ++c)
+    if (c < nch) load_chunk(c, j_begin + c * BN);
 
   f32x16 o[DB];
 #pragma unroll
@@ -157,23 +173,21 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
 
   auto chunk = [&](int t, const int st) {
     const int j0 = j_begin + t * BN;
-    // Chunk t+2 goes into the stage chunk t-1 used; then wait for chunk t (the
-    // loads of a wave complete in issue order, so "all but the newest n").
-    if (t + 2 < nch) {
-      load_chunk((st + 2) % 3, j0 + 2 * BN);
-      dma_wait_allbut<2 * LPC>();
-    } else if (t + 1 < nch) {
-      dma_wait_allbut<LPC>();
-    } else {
-      dma_wait();
-    }
+    // Chunk t + NST - 1 goes into the stage chunk t - 1 used; then wait for
+    // chunk t (the loads of a wave complete in issue order, so "all but the
+    // newest n").
+    if (t + NST - 1 < nch) load_chunk((st + NST - 1) % NST, j0 + (NST - 1) * BN);
+    const int after = min(NST - 1, nch - 1 - t);  // chunks issued after chunk t
+    if (after >= NST - 1) dma_wait_allbut<(NST - 1) * LPC>();
+    else if (NST > 4 && after == 3) dma_wait_allbut<3 * LPC>();
+    else if (NST > 3 && after == 2) dma_wait_allbut<2 * LPC>();
+    else if (after == 1) dma_wait_allbut<LPC>();
+    else dma_wait();
     const lds_t* Kt = kst(st);
     const lds_t* Vt = vst(st);
     f32x4 ksc[4], vsc[4];  // FP8: token scales of this lane's 16 keys
     if constexpr (KV8) {
-      widen_fp8_tile<D, BN, F16>(lds_base(kb_), Kt, lane);
       widen_fp8_tile<D, BN, F16>(lds_base(vb_), Vt, lane);
-      Kt = lds_base(kb_);
       Vt = lds_base(vb_);
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
@@ -181,9 +195,13 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
         vsc[gq] = *(const f32x4*)&vs_[st][gq * 8 + hi * 4];
       }
     }
-    f32x16 sc = mfma32x32x16_z<F16>(row_operand<D>(Kt, 0, 0, lane), qr[0]);
+    auto kop = [&](int ds) {
+      if constexpr (KV8) return fp8_row_operand<D, F16>(Kt, ds, lane);
+      else return row_operand<D>(Kt, 0, ds * 2, lane);
+    };
+    f32x16 sc = mfma32x32x16_z<F16>(kop(0), qr[0]);
 #pragma unroll
-    for (int ds = 1; ds < DS; ++ds) sc = mfma32x32x16<F16>(row_operand<D>(Kt, 0, ds * 2, lane), qr[ds], sc);
+    for (int ds = 1; ds < DS; ++ds) sc = mfma32x32x16<F16>(kop(ds), qr[ds], sc);
     if constexpr (KV8) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[i] *= ksc[i >> 2][i & 3];
@@ -227,10 +245,10 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
       o[db] = mfma32x32x16<F16>(tr_operand<D>(Vt, 16, db * 32, lane), p1, o[db]);
     }
   };
-  for (int t = 0; t < nch; t += 3) {
-    chunk(t, 0);
-    if (t + 1 < nch) chunk(t + 1, 1);
-    if (t + 2 < nch) chunk(t + 2, 2);
+  for (int t = 0; t < nch; t += NST) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+      if (t + st < nch) chunk(t + st, st);
   }
 
   // Partial state of this split: m in log2 units (m_ref * scale * log2 e), the
