@@ -44,7 +44,7 @@ namespace attn {
 
 namespace {
 
-constexpr float kLazyRescaleDec = 8.0f;  // log2 of the largest unnormalised weight
+constexpr float kLazyRescaleDecW = 256.0f;  // largest unnormalised weight kept without rescaling
 
 // Two E4M3 bytes (the low or high half of w) widened exactly to the 16-bit
 // format (every E4M3 value is representable in bf16 and in fp16). The scale
@@ -212,12 +212,34 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[i] = ((i >> 2) * 8 + (i & 3)) <= lim ? sc[i] : -INFINITY;
     }
-    float mx = max3f(sc[0], sc[1], sc[2]);
+    auto chunk_max = [&](const f32x16& x) {
+      float mx = max3f(x[0], x[1], x[2]);
 #pragma unroll
-    for (int i = 3; i < 15; i += 2) mx = max3f(mx, sc[i], sc[i + 1]);
-    mx = max_halves(fmaxf(mx, sc[15]));
-    if (__builtin_amdgcn_ballot_w64((mx - m_ref) * c2 > kLazyRescaleDec)) {
-      const float m_new = fmaxf(m_ref, mx);
+      for (int i = 3; i < 15; i += 2) mx = max3f(mx, x[i], x[i + 1]);
+      return max_halves(fmaxf(mx, x[15]));
+    };
+    auto weights = [&](f32x16& x) {
+      const float mc = m_ref * c2;
+      float sa = 0.f, sb = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        x[i] = fast_exp2(fmaf(x[i], c2, -mc));
+        x[i + 1] = fast_exp2(fmaf(x[i + 1], c2, -mc));
+        sa += x[i];
+        sb += x[i + 1];
+      }
+      return sa + sb;
+    };
+    // The split's first chunk sets the reference max (a column that sees none
+    // of its keys keeps the initial value and gets zero weights). Later chunks
+    // are weighted against the reference without taking their max; a weight
+    // above 2^8 forces the lane's partial sum above 2^8, and only then (rare)
+    // does the reference move to the exact max, rescaling O and l.
+    if (t == 0) m_ref = fmaxf(m_ref, chunk_max(sc));
+    const f32x16 raw = sc;
+    float sum = weights(sc);
+    if (__builtin_amdgcn_ballot_w64(!(sum <= kLazyRescaleDecW))) {
+      const float m_new = fmaxf(m_ref, chunk_max(raw));
       const float alpha = fast_exp2((m_ref - m_new) * c2);
       l_part *= alpha;
 #pragma unroll
@@ -225,13 +247,8 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
       m_ref = m_new;
-    }
-    const float mc = m_ref * c2;
-    float sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sc[i] = fast_exp2(fmaf(sc[i], c2, -mc));
-      sum += sc[i];
+      sc = raw;
+      sum = weights(sc);
     }
     l_part += sum;
     if constexpr (KV8) {
