@@ -51,11 +51,25 @@ def cpu_baseline(x, w, budget_s: float):
             break
     el = time.perf_counter() - t0
     flops = fwd_flops(1, 1, w.N, w.d, w.causal) * done
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"fp64 numpy oracle (three-pass softmax, S and P materialised) on {done} of "
                       f"{len(heads)} (b,h) heads of {WORKLOAD}; {el:.1f} s; host cpu_count="
-                      f"{os.cpu_count()}"}
+                      f"{os.cpu_count()} ({model}), BLAS threads={threads}"}
+
+
+def device_info(torch):
+    """Name, architecture and compute-unit count as the runtime reports them."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2**30, 1)}
 
 
 COPY_BYTES = 256 << 20
@@ -341,6 +355,7 @@ def main():
         "config": {"workload": WORKLOAD, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "device": device_info(torch),
         "kernel_ms": {"mean": round(mean_ms, 4), "median": round(median_ms, 4),
                       "p90": round(per[int(0.9 * (len(per) - 1))], 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
