@@ -78,6 +78,29 @@ def test_decode_matches_forward_rows():
     assert_close(l_d, l_f[:, :, N - 8:].cpu().double().numpy(), LSE_TOL["bf16"], "decode vs fwd LSE")
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8kv"])
+def test_decode_rising_scores(fp8):
+    """Scores grow by 8 per 32-key chunk (11.5 in log2 units, above the 2^8
+    weight bound), so every chunk of every split moves the reference max and
+    rescales its partial state before the merge."""
+    B, H, H_kv, Nq, Nk, d = 2, 8, 2, 3, 700, 128
+    x = make_inputs(B, H, Nk, d, torch.bfloat16, seed=93, H_kv=H_kv, Nq=Nq, std=0.05)
+    q, k = x["q"].float(), x["k"].float()
+    q[..., 0] = 1.0
+    k[..., 0] = 0.25 * torch.arange(Nk, dtype=torch.float32)
+    x["q"], x["k"] = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    x["v"] = make_inputs(B, H, Nk, d, torch.bfloat16, seed=94, H_kv=H_kv, Nq=Nq)["v"]
+    if fp8:
+        k8, v8, ks, vs, kd, vd = _fp8_case(x)
+        o, lse = run_decode_fp8(x["q"], k8, v8, ks, vs, 1.0, True, num_splits=3)
+        ro, rl = oracle.attn_ref_decode(x["q"], kd, vd, 1.0, True)
+    else:
+        o, lse = run_decode(x, 1.0, True, num_splits=3)
+        ro, rl = oracle.attn_ref_decode(x["q"], x["k"], x["v"], 1.0, True)
+    assert_close(o, ro, O_TOL["bf16"], "rising decode O")
+    assert_close(lse, rl, LSE_TOL["bf16"], "rising decode LSE")
+
+
 def test_decode_split_invariance():
     """The split count changes only the rounding of the merge."""
     x = make_inputs(2, 8, 3000, 128, torch.bfloat16, seed=63, H_kv=2, Nq=2)

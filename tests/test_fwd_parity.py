@@ -202,6 +202,35 @@ def test_f16_large_values(d):
     assert_close(lse, rl, LSE_TOL["f16"], "f16 large values LSE")
 
 
+def rising_scores(B, H, N, d, dtype, step, seed):
+    """Inputs whose scores rise along the keys: q . k_j = step * j plus small
+    noise, so every key tile's scores lie far above the previous tiles' max and
+    the online softmax has to move its reference max on every tile."""
+    x = make_inputs(B, H, N, d, dtype, seed=seed, std=0.05)
+    x["q"] = x["q"].float()
+    x["k"] = x["k"].float()
+    x["q"][..., 0] = 1.0
+    x["k"][..., 0] = step * torch.arange(N, dtype=torch.float32)
+    x["q"] = x["q"].to(dtype)
+    x["k"] = x["k"].to(dtype)
+    x["v"] = make_inputs(B, H, N, d, dtype, seed=seed + 1)["v"]
+    return x
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
+def test_rising_scores_move_the_reference(causal, dtype):
+    """Scores grow by 16 per 64-key tile (23 in log2 units, above the 2^8
+    weight bound), so every tile takes the rescaling path of the online
+    softmax ([SafeSoftmax] §3.2): O and LSE must still match the oracle."""
+    x = rising_scores(2, 2, 333, 128, dtype, 0.25, seed=91)
+    o, lse = run_fwd(x["q"], x["k"], x["v"], 1.0, causal)
+    ro, rl = oracle.attn_ref_fwd(x["q"], x["k"], x["v"], 1.0, causal)
+    dn = dtype_name(x["q"])
+    assert_close(o, ro, O_TOL[dn], "rising scores O")
+    assert_close(lse, rl, LSE_TOL[dn], "rising scores LSE")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
 def test_padding_contents_never_read(causal, dtype):
