@@ -58,7 +58,8 @@ DecodePlan decode_plan(int B, int H, int H_kv, int Nq, int Nk, int num_splits) {
   p.col_groups = ((H / H_kv) * Nq + 31) / 32;
   long long want = num_splits;
   if (want <= 0) {
-    const long long units = (long long)B * H_kv * p.col_groups;
+    // About 768 workgroups: one resident round at the decode kernel's LDS use.
+    const long long units = (long long)B * H_kv * (p.col_groups / attn::decode_waves(p.col_groups));
     want = (768 + units - 1) / units;
   }
   const long long max_splits = (Nk + 31) / 32;

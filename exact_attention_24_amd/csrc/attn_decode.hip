@@ -96,30 +96,34 @@ __device__ __forceinline__ e16x8 fp8_row_operand(const lds_t* tile, int ds, int 
   return as_e16x8(e);
 }
 
-template <int D, bool F16, bool KV8>
+template <int D, bool F16, bool KV8, int NW>
 __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   constexpr int BN = 32;  // keys per chunk
   constexpr int DD = KV8 ? D / 2 : D;  // row width in 16-bit units as stored in HBM
   constexpr int TILE = BN * DD * 2;    // bytes of one stored chunk
   constexpr int DS = D / 16, DB = D / 32;
-  constexpr int LPC = 2 * TileDma<DD, BN, 1>::ITER + (KV8 ? 2 : 0);  // loads per chunk
+  constexpr int LPC = 2 * TileDma<DD, BN, NW>::ITER + (KV8 ? 2 : 0);  // loads per chunk and wave
   // Ring of NST chunk stages, NST - 1 chunks in flight. An FP8 chunk is half
   // the bytes of a 16-bit one, so its ring is deeper: both keep about 32 KiB
   // per wave in flight (a split is bound by its loads' latency, not by HBM).
   constexpr int NST = KV8 ? 5 : 3;
   __shared__ __attribute__((aligned(1024))) char kr_[NST][TILE], vr_[NST][TILE];
   // FP8 only: per-stage token scales (64 floats fetched, the first 32 used)
-  // and the 16-bit tile V is widened into (K is widened in registers).
+  // and, per wave, the 16-bit tile V is widened into (K is widened in
+  // registers).
   __shared__ __attribute__((aligned(256))) float ks_[KV8 ? NST : 1][64], vs_[KV8 ? NST : 1][64];
-  __shared__ __attribute__((aligned(1024))) char vb_[KV8 ? BN * D * 2 : 16];
+  __shared__ __attribute__((aligned(1024))) char vb_[KV8 ? NW : 1][KV8 ? BN * D * 2 : 16];
 
-  const int lane = threadIdx.x, l32 = lane & 31, hi = lane >> 5;
+  // NW waves share each chunk: wave w takes column block cg0 + w of the same
+  // (batch, K/V head, split), so the chunk is fetched once for all of them.
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int G = a.H / a.H_kv;
   int bid = blockIdx.x;
   const int s = bid % a.splits;
   bid /= a.splits;
-  const int cg = bid % a.col_groups;
-  bid /= a.col_groups;
+  const int cg = (bid % (a.col_groups / NW)) * NW + wave;
+  bid /= a.col_groups / NW;
   const int bkv = bid;  // b * H_kv + kv head
   const int b = bkv / a.H_kv, kvh = bkv % a.H_kv;
   const int L = a.kv_lens ? min(max(a.kv_lens[b], 0), a.Nk) : a.Nk;
@@ -143,8 +147,8 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
     qr[ds] = as_e16x8(cvalid ? gload16((const e16_t*)a.q + qrow * D + ds * 16 + hi * 8) : zero4);
 
   const size_t kvoff = (size_t)bkv * a.Nk * DD;  // in 16-bit units
-  const TileDma<DD, BN, 1> kdma((const e16_t*)a.k + kvoff, j_end, 0, lane);
-  const TileDma<DD, BN, 1> vdma((const e16_t*)a.v + kvoff, j_end, 0, lane);
+  const TileDma<DD, BN, NW> kdma((const e16_t*)a.k + kvoff, j_end, wave, lane);
+  const TileDma<DD, BN, NW> vdma((const e16_t*)a.v + kvoff, j_end, wave, lane);
   auto kst = [&](int st) { return lds_base(kr_[st]); };
   auto vst = [&](int st) { return lds_base(vr_[st]); };
   const float* ksh = KV8 ? a.k_scale + (size_t)bkv * a.Nk : nullptr;
@@ -152,7 +156,7 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   auto load_chunk = [&](int st, int j0) {
     kdma.load(kst(st), j0);
     vdma.load(vst(st), j0);
-    if constexpr (KV8) {
+    if constexpr (KV8) {  // every wave fetches the same scales to the same place
       vec64_dma(lds_base((char*)ks_[st]), ksh, j_end, j0, lane);
       vec64_dma(lds_base((char*)vs_[st]), vsh, j_end, j0, lane);
     }
@@ -173,22 +177,29 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
 
   auto chunk = [&](int t, const int st) {
     const int j0 = j_begin + t * BN;
-    // Chunk t + NST - 1 goes into the stage chunk t - 1 used; then wait for
-    // chunk t (the loads of a wave complete in issue order, so "all but the
-    // newest n").
-    if (t + NST - 1 < nch) load_chunk((st + NST - 1) % NST, j0 + (NST - 1) * BN);
-    const int after = min(NST - 1, nch - 1 - t);  // chunks issued after chunk t
-    if (after >= NST - 1) dma_wait_allbut<(NST - 1) * LPC>();
-    else if (NST > 4 && after == 3) dma_wait_allbut<3 * LPC>();
-    else if (NST > 3 && after == 2) dma_wait_allbut<2 * LPC>();
+    // Chunk t + NST - 1 goes into the stage chunk t - 1 used; chunk t is
+    // waited for (the loads of a wave complete in issue order, so "all but the
+    // newest n"). One wave: issue first, then wait. Several: wait for this
+    // wave's share of chunk t, meet at the barrier (every share has landed and
+    // every wave is done with chunk t - 1), then issue.
+    const bool more = t + NST - 1 < nch;
+    if (NW == 1 && more) load_chunk((st + NST - 1) % NST, j0 + (NST - 1) * BN);
+    const int after = min(NW == 1 ? NST - 1 : NST - 2, nch - 1 - t);  // chunks issued after t
+    if (after >= 4) dma_wait_allbut<(NST > 4 ? 4 : 1) * LPC>();
+    else if (after == 3) dma_wait_allbut<(NST > 3 ? 3 : 1) * LPC>();
+    else if (after == 2) dma_wait_allbut<2 * LPC>();
     else if (after == 1) dma_wait_allbut<LPC>();
     else dma_wait();
+    if constexpr (NW > 1) {
+      __syncthreads();
+      if (more) load_chunk((st + NST - 1) % NST, j0 + (NST - 1) * BN);
+    }
     const lds_t* Kt = kst(st);
     const lds_t* Vt = vst(st);
     f32x4 ksc[4], vsc[4];  // FP8: token scales of this lane's 16 keys
     if constexpr (KV8) {
-      widen_fp8_tile<D, BN, F16>(lds_base(vb_), Vt, lane);
-      Vt = lds_base(vb_);
+      widen_fp8_tile<D, BN, F16>(lds_base(vb_[wave]), Vt, lane);
+      Vt = lds_base(vb_[wave]);
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         ksc[gq] = *(const f32x4*)&ks_[st][gq * 8 + hi * 4];
@@ -291,9 +302,9 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
 
 // Thin __global__ wrapper (the host pass drops launch stubs of __global__
 // templates whose body holds the buffer-load builtins directly).
-template <int D, bool F16, bool KV8>
-__global__ void __launch_bounds__(64) decode_split_kernel(DecArgs a) {
-  decode_split_body<D, F16, KV8>(a);
+template <int D, bool F16, bool KV8, int NW>
+__global__ void __launch_bounds__(64 * NW) decode_split_kernel(DecArgs a) {
+  decode_split_body<D, F16, KV8, NW>(a);
 }
 
 // Merge the splits of one query row ([SafeSoftmax] §3.2): with M = max_s m_s,
@@ -327,8 +338,13 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
 
 template <int D, bool F16, bool KV8>
 hipError_t launch_decode_t(const DecArgs& a, hipStream_t stream) {
-  const unsigned wgs = (unsigned)(a.B * a.H_kv * a.col_groups * a.splits);
-  hipLaunchKernelGGL((decode_split_kernel<D, F16, KV8>), dim3(wgs), dim3(64), 0, stream, a);
+  // Two waves per workgroup share the K/V chunks when the column blocks pair up.
+  const int nw = decode_waves(a.col_groups);
+  const unsigned wgs = (unsigned)(a.B * a.H_kv * (a.col_groups / nw) * a.splits);
+  if (nw == 2)
+    hipLaunchKernelGGL((decode_split_kernel<D, F16, KV8, 2>), dim3(wgs), dim3(128), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, F16, KV8, 1>), dim3(wgs), dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D, F16>), dim3((unsigned)(a.B * a.H * a.Nq)), dim3(D), 0,

@@ -61,6 +61,10 @@ struct DecArgs {
   float scale, scale_log2;
 };
 
+// Waves per decode workgroup: two column blocks of the same (batch, K/V head,
+// split) share one workgroup (and each fetched chunk) when they pair up.
+inline int decode_waves(int col_groups) { return col_groups % 2 == 0 ? 2 : 1; }
+
 // Each launcher enqueues its kernels on `stream` and returns the launch status.
 // 16-bit formats: bf16, or fp16 when f16 is set.
 hipError_t launch_fwd_16(const FwdArgs& a, int d, bool causal, bool f16, hipStream_t stream);

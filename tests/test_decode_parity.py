@@ -24,9 +24,12 @@ DEV = "cuda:0"
 
 # (B, H, H_kv, Nq, Nk, d): one token against a ragged cache; 5 tokens, MHA;
 # 4 tokens x group 4 = 16 columns; MQA with 16 heads x 4 tokens = 64 columns
-# (two column blocks); 16 tokens over 129 keys
+# (two column blocks, one two-wave workgroup); 16 tokens over 129 keys; MQA
+# with 32 heads x 4 tokens = 128 columns (two two-wave workgroups); 3 tokens x
+# group 32 = 96 columns (three column blocks, one wave each)
 SHAPES = [(2, 8, 2, 1, 300, 128), (1, 4, 4, 5, 700, 64), (3, 32, 8, 4, 1000, 128),
-          (1, 16, 1, 4, 333, 128), (2, 2, 2, 16, 129, 64)]
+          (1, 16, 1, 4, 333, 128), (2, 2, 2, 16, 129, 64), (1, 32, 1, 4, 500, 128),
+          (2, 64, 2, 3, 260, 64)]
 
 
 def run_decode(x, scale, causal, kv_lens=None, num_splits=0):
