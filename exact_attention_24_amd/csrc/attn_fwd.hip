@@ -57,6 +57,22 @@ namespace {
 // ----------------------------------------------------------------------------
 constexpr float kLazyRescaleW = 256.0f;  // largest unnormalised weight kept without rescaling
 
+// The batch index of the sequence at position `rank` in the order of
+// decreasing length (ties: lower index first), for B <= 64: lane j holds
+// sequence j's length and counts the sequences ahead of it. Same result in
+// every lane and wave.
+__device__ __forceinline__ int batch_of_rank(const int32_t* seqlens, int B, int N, int rank) {
+  const int lane = threadIdx.x & 63;
+  const int len = lane < B ? min(max(seqlens[lane], 0), N) : -1;
+  int ahead = 0;
+  for (int j = 0; j < B; ++j) {
+    const int lj = __builtin_amdgcn_readlane(len, j);
+    ahead += (lj > len) | ((lj == len) & (j < lane));
+  }
+  const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < B && ahead == rank);
+  return __builtin_ffsll((long long)hit) - 1;
+}
+
 template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void fwd_16_body(const FwdArgs& a) {
   constexpr int BM = 128, BN = 64;
@@ -78,7 +94,14 @@ __device__ __forceinline__ void fwd_16_body(const FwdArgs& a) {
   const int N = a.N;
   const int nm = (N + BM - 1) / BM;
   int bh, mt;
-  tile_order(blockIdx.x, nm, a.B * a.H, a.H / a.H_kv, CAUSAL, bh, mt);
+  const int group = a.H / a.H_kv;
+  if (a.seqlens && a.B <= 64 && ((a.H / group) & 7) == 0) {
+    int rank, h;
+    varlen_order(blockIdx.x, nm, a.H, group, CAUSAL, rank, h, mt);
+    bh = batch_of_rank(a.seqlens, a.B, N, rank) * a.H + h;
+  } else {
+    tile_order(blockIdx.x, nm, a.B * a.H, group, CAUSAL, bh, mt);
+  }
   const int b = bh / a.H;
   int L = N;
   if (a.seqlens) L = min(max(a.seqlens[b], 0), N);

@@ -32,4 +32,23 @@ __host__ __device__ inline void tile_order(int block, int num_tiles, int num_hea
   tile = heavy_first ? num_tiles - 1 - r : r;
 }
 
+// Padded batches (per-sequence lengths on the device): a workgroup's run time
+// grows with its sequence's length, so the longest sequences go first. Block
+// b maps to (rank, head, tile): rank is the position of the sequence in the
+// order of decreasing length (the caller turns it into a batch index), and
+// within one rank the heads and tiles are laid out as in tile_order above
+// (XCD b % 8 holds the same heads of every sequence; heavy_first puts each
+// head's last tile first). Needs num_heads / group to be a multiple of 8.
+__host__ __device__ inline void varlen_order(int block, int num_tiles, int num_heads, int group,
+                                             bool heavy_first, int& rank, int& head, int& tile) {
+  const int xcd = block & 7, slot = block >> 3;
+  const int heads_per_xcd = num_heads >> 3;
+  const int per_rank = heads_per_xcd * num_tiles;
+  rank = slot / per_rank;
+  const int rem = slot % per_rank;
+  const int r = rem / heads_per_xcd, s = rem % heads_per_xcd;
+  head = ((s / group) * 8 + xcd) * group + s % group;
+  tile = heavy_first ? num_tiles - 1 - r : r;
+}
+
 }  // namespace attn

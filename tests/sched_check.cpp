@@ -39,7 +39,39 @@ static int check(int tiles, int heads, int group, int seq_heads, bool heavy) {
   return 0;
 }
 
+// varlen_order: a bijection onto (rank, head, tile); ranks in launch order;
+// each (rank, head) on one XCD, grouped heads together; heavy-first within a
+// rank.
+static int check_varlen(int tiles, int B, int heads, int group, bool heavy) {
+  const int n = B * heads * tiles;
+  std::vector<int> seen(n, 0), xcd(B * heads, -1);
+  int last_rank = 0;
+  for (int b = 0; b < n; ++b) {
+    int r, h, t;
+    attn::varlen_order(b, tiles, heads, group, heavy, r, h, t);
+    if (r < 0 || r >= B || h < 0 || h >= heads || t < 0 || t >= tiles) { printf("varlen out of range %d\n", b); return 1; }
+    if (seen[(r * heads + h) * tiles + t]++) { printf("varlen duplicate (%d,%d,%d)\n", r, h, t); return 1; }
+    if (r < last_rank) { printf("varlen rank order at %d\n", b); return 1; }
+    last_rank = r > last_rank ? r : last_rank;
+    if (xcd[r * heads + h] == -1) xcd[r * heads + h] = b % 8;
+    if (xcd[r * heads + h] != b % 8) { printf("varlen head on two XCDs\n"); return 1; }
+    if (xcd[r * heads + (h / group) * group] != -1 && xcd[r * heads + (h / group) * group] != b % 8) {
+      printf("varlen group split\n"); return 1;
+    }
+    const int first_of_rank = r * heads * tiles;
+    if (heavy && b - first_of_rank < heads && t != tiles - 1) { printf("varlen heavy-first at %d\n", b); return 1; }
+  }
+  return 0;
+}
+
 int main() {
+  const int vcases[][4] = {{16, 8, 16, 1}, {32, 3, 32, 4}, {5, 7, 8, 1}, {1, 2, 64, 8}};
+  for (const auto& c : vcases)
+    for (int heavy = 0; heavy < 2; ++heavy)
+      if (check_varlen(c[0], c[1], c[2], c[3], heavy)) {
+        printf("varlen case tiles=%d B=%d heads=%d group=%d heavy=%d\n", c[0], c[1], c[2], c[3], heavy);
+        return 1;
+      }
   const int cases[][4] = {{16, 128, 1, 16}, {32, 64, 1, 32}, {16, 64, 4, 32}, {7, 24, 3, 24},
                           {5, 12, 1, 6}, {1, 8, 8, 8}, {64, 32, 1, 16}, {3, 48, 2, 48}};
   for (const auto& c : cases)
