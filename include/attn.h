@@ -180,9 +180,11 @@ size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d
  *            L_b - Nq .. L_b - 1; with causal != 0 query i sees keys
  *            j <= L_b - Nq + i (with Nq = L_b: the mask of attn_fwd), otherwise
  *            every valid key. A query that sees no key gets O = 0, LSE = -inf.
- *  num_splits  key-range splits per (batch, K/V head); 0 picks about 768
- *            single-wave workgroups in all (one resident round on MI355X).
- *            Results do not depend on it beyond rounding.
+ *  num_splits  key-range splits per (batch, K/V head); 0 picks a count
+ *            that gives about 512 workgroups for one-wave workgroups over a
+ *            16-bit cache and about 768 otherwise (FP8 cache, or query
+ *            columns in pairs of 32-column blocks, whose workgroups hold two
+ *            waves). Results do not depend on it beyond rounding.
  *  workspace device buffer of attn_decode_workspace_bytes(...) bytes, 256-byte
  *            aligned; contents on entry are ignored.
  *
