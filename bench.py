@@ -64,12 +64,29 @@ def cpu_baseline(x, w, budget_s: float):
                       f"{os.cpu_count()} ({model}), BLAS threads={threads}"}
 
 
+def max_sclk_mhz():
+    """Highest shader-clock level the driver lists (amdgpu sysfs), or None."""
+    import glob
+    import re
+    best = None
+    for path in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+        try:
+            with open(path) as f:
+                for m in re.finditer(r"(\d+)\s*[Mm][Hh]z", f.read()):
+                    best = max(best or 0, int(m.group(1)))
+        except OSError:
+            continue
+    return best
+
+
 def device_info(torch):
-    """Name, architecture and compute-unit count as the runtime reports them."""
+    """Name, architecture, compute-unit count and top clock level as the
+    runtime and driver report them."""
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
             "compute_units": p.multi_processor_count,
-            "hbm_gib": round(p.total_memory / 2**30, 1)}
+            "hbm_gib": round(p.total_memory / 2**30, 1),
+            "max_sclk_mhz": max_sclk_mhz()}
 
 
 COPY_BYTES = 256 << 20

@@ -54,11 +54,15 @@ def test_decode_small(shape, causal, dtype, splits):
     assert_close(lse, rl, LSE_TOL[dn], f"decode{shape} LSE")
 
 
+@pytest.mark.parametrize("heads", [(8, 2), (32, 2)], ids=["one_wave", "two_waves"])
 @pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
-def test_decode_kv_lens(causal):
+def test_decode_kv_lens(causal, heads):
     """Per-sequence cache lengths: empty, one key, fewer keys than queries (the
-    earliest queries then see nothing under the causal mask), ragged, full."""
-    B, H, H_kv, Nq, Nk, d = 6, 8, 2, 4, 500, 128
+    earliest queries then see nothing under the causal mask), ragged, full.
+    With 32 query heads over 2 K/V heads the 64 columns run as a two-wave
+    workgroup."""
+    H, H_kv = heads
+    B, Nq, Nk, d = 6, 4, 500, 128
     x = make_inputs(B, H, Nk, d, torch.bfloat16, seed=61 + causal, H_kv=H_kv, Nq=Nq)
     lens = torch.tensor([0, 1, 3, 257, 500, 64], dtype=torch.int32)
     o, lse = run_decode(x, 1 / math.sqrt(d), causal, lens, num_splits=4)
