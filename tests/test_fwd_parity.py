@@ -149,6 +149,19 @@ def test_small_varlen(d, causal, dtype):
     check_full(x, 1 / math.sqrt(d), causal, f"varlen d={d}")
 
 
+@pytest.mark.parametrize("heads", [(8, 8), (16, 8)], ids=["mha", "gqa"])
+@pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
+def test_varlen_length_order(causal, heads):
+    """A padded batch whose head count lets the kernel launch sequences in
+    order of decreasing length (ties included: the order must still cover
+    every (sequence, head, tile) exactly once); every row checked."""
+    H, H_kv = heads
+    B, N, d = 7, 300, 128
+    x = make_inputs(B, H, N, d, torch.bfloat16, seed=79 + causal, H_kv=H_kv)
+    x["seqlens"] = torch.tensor([37, 300, 0, 150, 300, 1, 150], dtype=torch.int32)
+    check_full(x, 1 / math.sqrt(d), causal, "length-ordered varlen")
+
+
 # ------------------------------------------------ full workloads, sampled rows
 
 FWD_WORKLOADS = [n for n, w in WORKLOADS.items() if w.Nq is None]  # decode has its own test
