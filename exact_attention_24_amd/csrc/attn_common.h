@@ -72,6 +72,16 @@ __device__ __forceinline__ u32x2 lds_load_tr16(const lds_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Transposing LDS read of eight 8-bit values. Within each group of 16 lanes,
+// let M[src][b] be the eight bytes at lane src's address; lane j receives
+// M[(j >> 3) + 2*s][j & 7] as its byte s, s = 0..7 (layout measured on the
+// device with an in-bounds probe).
+__device__ __forceinline__ u32x2 lds_load_tr8(const lds_t* p) {
+  typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+  i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((ATTN_LDS i32x2*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
 __device__ __forceinline__ e16x8 join_e16x8(u32x2 lo, u32x2 hi) {
   u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
   return as_e16x8(v);

@@ -14,19 +14,22 @@
 // (m, l, unnormalised O) of [SafeSoftmax] §3.1 for its keys, and a second
 // kernel combines the splits with the merge rule of [SafeSoftmax] §3.2.
 //
-// Split kernel: one wave per workgroup. The G = H / H_kv query heads that
-// share a K/V head ([OpOpt] §五) and their N_q queries are packed into the 32
-// columns of one MFMA block (column c = g*N_q + i), so each K/V byte is read
-// from HBM once for all of them. K/V chunks of 32 keys stream through a
-// per-wave three-stage ring in LDS by direct buffer->LDS loads, two chunks in
-// flight ahead of the one being computed; S^T = K Q^T and O^T += V^T P^T run
-// on v_mfma_f32_32x32x16 exactly as in the forward kernel.
+// Split kernel: one wave per 32-column block. The G = H / H_kv query heads
+// that share a K/V head ([OpOpt] §五) and their N_q queries are packed into
+// the columns of MFMA blocks (column c = g*N_q + i, 32 per block), so each K/V
+// byte is read from HBM once for all of them; two blocks of the same (batch,
+// K/V head, split) run as the two waves of one workgroup and share every
+// chunk load. K/V chunks of 32 keys stream through a ring in LDS by direct
+// buffer->LDS loads (three stages, two chunks in flight; FP8: five stages,
+// four in flight, the same bytes); S^T = K Q^T and O^T += V^T P^T run on
+// v_mfma_f32_32x32x16 exactly as in the forward kernel.
 //
 // FP8 K/V cache ([OpOpt] §六): K and V stored as OCP E4M3 bytes with one fp32
-// scale per token (K_j = k8_j * ks_j, V_j = v8_j * vs_j). HBM carries the
-// 8-bit form; each chunk is widened to the 16-bit format of Q in LDS (every
-// E4M3 value is exact in bf16 and in fp16) and the products run on the
-// matching MFMA. The scales are applied in fp32:
+// scale per token (K_j = k8_j * ks_j, V_j = v8_j * vs_j). HBM and LDS carry the
+// 8-bit form; each MFMA operand is read from the FP8 tile (V through the 8-bit
+// transposing read) and widened exactly to the 16-bit format of Q in
+// registers (every E4M3 value is exact in bf16 and in fp16), and the products
+// run on the matching MFMA. The scales are applied in fp32:
 // ks_j to the scores after the K product (S_ij = ks_j * (q_i . k8_j)), vs_j
 // to the weights before they are rounded for the V product (the row sums use
 // the unscaled weights), so the softmax and accumulation stay fp32.
@@ -59,31 +62,6 @@ __device__ __forceinline__ uint32_t widen2(uint32_t w, bool high) {
                                              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false));
 }
 
-// Widen one chunk of FP8 rows (BN rows of D bytes, laid out by TileDma<D/2>:
-// 16-byte chunk c of row r at c ^ swz<D/2>(r)) into a 16-bit tile in the
-// forward's swizzled layout. Lane l converts half l&1 of row l>>1.
-template <int D, int BN, bool F16>
-__device__ __forceinline__ void widen_fp8_tile(lds_t* dst, const lds_t* src, int lane) {
-  static_assert(BN * 2 == 64, "one lane per half row");
-  const int r = lane >> 1, half = lane & 1;
-  constexpr int C8 = D / 16;  // 16-byte chunks per fp8 row
-#pragma unroll
-  for (int i = 0; i < C8 / 2; ++i) {
-    const int c8 = half * (C8 / 2) + i;
-    const u32x4 w = lds_load16(src + r * D + ((c8 ^ swz<D / 2>(r)) << 4));
-    u32x4 lo, hi;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      lo[2 * j + 0] = widen2<F16>(w[j], false);
-      lo[2 * j + 1] = widen2<F16>(w[j], true);
-      hi[2 * j + 0] = widen2<F16>(w[2 + j], false);
-      hi[2 * j + 1] = widen2<F16>(w[2 + j], true);
-    }
-    lds_store16(dst + tile_off<D>(r, 2 * c8), lo);
-    lds_store16(dst + tile_off<D>(r, 2 * c8 + 1), hi);
-  }
-}
-
 // A operand of the score MFMA for k step ds, straight from an FP8 tile in the
 // layout above: lane l takes key row l%32, bytes 16*ds + 8*(l/32) .. +7 (eight
 // consecutive d), widened exactly in registers (no 16-bit copy of K in LDS).
@@ -91,6 +69,24 @@ template <int D, bool F16>
 __device__ __forceinline__ e16x8 fp8_row_operand(const lds_t* tile, int ds, int lane) {
   const int r = lane & 31;
   const u32x2 w = lds_load8(tile + r * D + ((ds ^ swz<D / 2>(r)) << 4) + (lane >> 5) * 8);
+  const u32x4 e = {widen2<F16>(w[0], false), widen2<F16>(w[0], true), widen2<F16>(w[1], false),
+                   widen2<F16>(w[1], true)};
+  return as_e16x8(e);
+}
+
+// A operand of the P V MFMA (V^T rows d = col0 + l%32, the 8 keys of 16-key
+// step row0 that the score accumulator lanes hold: row0 + hi*4 + {0..3} and
+// row0 + 8 + hi*4 + {0..3}) straight from an FP8 V tile, with one transposing
+// 8-bit read: source lane src of each 16-lane group addresses key slot src/2
+// at columns 8*(src%2) .. +7 of its 16-column half, and lane j receives the
+// byte (j%16)%8 of sources (j%16)/8 + 2s, i.e. column col0 + l%32 of key slot
+// s. Widened exactly in registers.
+template <int D, bool F16>
+__device__ __forceinline__ e16x8 fp8_tr_operand(const lds_t* tile, int row0, int col0, int lane) {
+  const int g = lane >> 4, src = lane & 15, s = src >> 1;
+  const int key = row0 + (s < 4 ? (g >> 1) * 4 + s : 8 + (g >> 1) * 4 + (s - 4));
+  const int c = col0 + 16 * (g & 1) + 8 * (src & 1);
+  const u32x2 w = lds_load_tr8(tile + key * D + (((c >> 4) ^ swz<D / 2>(key)) << 4) + (c & 15));
   const u32x4 e = {widen2<F16>(w[0], false), widen2<F16>(w[0], true), widen2<F16>(w[1], false),
                    widen2<F16>(w[1], true)};
   return as_e16x8(e);
@@ -108,11 +104,9 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   // per wave in flight (a split is bound by its loads' latency, not by HBM).
   constexpr int NST = KV8 ? 5 : 3;
   __shared__ __attribute__((aligned(1024))) char kr_[NST][TILE], vr_[NST][TILE];
-  // FP8 only: per-stage token scales (64 floats fetched, the first 32 used)
-  // and, per wave, the 16-bit tile V is widened into (K is widened in
-  // registers).
+  // FP8 only: per-stage token scales (64 floats fetched, the first 32 used).
+  // K and V operands are widened in registers from the FP8 tiles.
   __shared__ __attribute__((aligned(256))) float ks_[KV8 ? NST : 1][64], vs_[KV8 ? NST : 1][64];
-  __shared__ __attribute__((aligned(1024))) char vb_[KV8 ? NW : 1][KV8 ? BN * D * 2 : 16];
 
   // NW waves share each chunk: wave w takes column block cg0 + w of the same
   // (batch, K/V head, split), so the chunk is fetched once for all of them.
@@ -198,8 +192,6 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
     const lds_t* Vt = vst(st);
     f32x4 ksc[4], vsc[4];  // FP8: token scales of this lane's 16 keys
     if constexpr (KV8) {
-      widen_fp8_tile<D, BN, F16>(lds_base(vb_[wave]), Vt, lane);
-      Vt = lds_base(vb_[wave]);
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         ksc[gq] = *(const f32x4*)&ks_[st][gq * 8 + hi * 4];
@@ -269,8 +261,13 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
     const e16x8 p0 = pack8<F16>(sc, 0), p1 = pack8<F16>(sc, 1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      o[db] = mfma32x32x16<F16>(tr_operand<D>(Vt, 0, db * 32, lane), p0, o[db]);
-      o[db] = mfma32x32x16<F16>(tr_operand<D>(Vt, 16, db * 32, lane), p1, o[db]);
+      if constexpr (KV8) {
+        o[db] = mfma32x32x16<F16>(fp8_tr_operand<D, F16>(Vt, 0, db * 32, lane), p0, o[db]);
+        o[db] = mfma32x32x16<F16>(fp8_tr_operand<D, F16>(Vt, 16, db * 32, lane), p1, o[db]);
+      } else {
+        o[db] = mfma32x32x16<F16>(tr_operand<D>(Vt, 0, db * 32, lane), p0, o[db]);
+        o[db] = mfma32x32x16<F16>(tr_operand<D>(Vt, 16, db * 32, lane), p1, o[db]);
+      }
     }
   };
   for (int t = 0; t < nch; t += NST) {
