@@ -27,15 +27,17 @@ namespace attn {
 namespace {
 
 // ----------------------------------------------------------------------------
-// bf16 inputs, MFMA products, fp32 softmax and accumulation.
+// 16-bit inputs (bf16, or fp16 with F16), MFMA products, fp32 softmax and
+// accumulation.
 //
 // Workgroup: 4 waves, 128 query rows (32 per wave), K/V tiles of 64 keys,
 // double-buffered in LDS and filled by direct global->LDS loads
 // (global_load_lds_dwordx4, no VGPR staging). Scores are computed transposed,
-// S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand and
-// Q (held in VGPRs for the whole loop) is the B operand, so each lane's
-// accumulator holds keys of ONE query. Row max and row sum are in-lane
-// operations plus one exchange between the two 32-lane halves. The output is
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (_f16): K (from LDS) is the A
+// operand and Q (held in VGPRs for the whole loop) is the B operand, so each
+// lane's accumulator holds keys of ONE query. Row reductions (sum, and the max
+// where one is taken) are in-lane operations plus one exchange between the two
+// 32-lane halves. The output is
 // accumulated transposed as well, O^T += V^T P^T: P^T stays in the lanes it was
 // computed in (B operand) and V^T is read from the row-major V tile with the
 // transposing LDS load, in the key order P^T's lanes hold.
