@@ -54,8 +54,18 @@ def test_status_strings(L):
 
 
 # Fake, 16-byte-aligned "device" addresses: never dereferenced, because every
-# call below fails validation first.
+# call below fails validation first. As a second guard these tests do not run
+# where a GPU is visible (a call that passed validation by mistake would launch
+# a kernel on them).
 P = 0x10000
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+cpu_only = pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: host-only checks")
 
 
 def fwd(L, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=64, d=64, dtype=1, scale=0.125, causal=0,
@@ -72,6 +82,7 @@ def fwd(L, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=64, d=64, dtype=1, scale=0.125
     (dict(q=P + 8), INVALID), (dict(o=P + 4), INVALID), (dict(lse=P + 2), INVALID),
     (dict(seqlens=P + 1), INVALID), (dict(B=1 << 20, H=1 << 12, N=1 << 12), UNSUPPORTED),
 ])
+@cpu_only
 def test_fwd_rejects_bad_arguments(L, kw, want):
     # scale and null-pointer checks come after size checks; each case fails exactly one rule
     assert fwd(L, **kw) == want
@@ -94,7 +105,9 @@ def bwd(L, ws_bytes=None, **kw):
     (dict(ws_bytes=16), INVALID), (dict(scale=0.0), INVALID), (dict(dtype=0), UNSUPPORTED),
     (dict(N=-5), INVALID),
 ])
+@cpu_only
 def test_bwd_rejects_bad_arguments(L, kw, want):
+    kw = dict(kw)
     ws_bytes = kw.pop("ws_bytes", None)
     assert bwd(L, ws_bytes, **kw) == want
 
@@ -107,11 +120,13 @@ def fwd_gqa(L, H=4, H_kv=2, **kw):
 
 
 @pytest.mark.parametrize("H,H_kv", [(4, 0), (4, -1), (4, 3), (4, 8), (6, 4)])
+@cpu_only
 def test_gqa_rejects_bad_head_counts(L, H, H_kv):
     assert fwd_gqa(L, H, H_kv, q=0) == INVALID  # still rejected (null q) ...
     assert fwd_gqa(L, H, H_kv) == INVALID       # ... and for the head count alone
 
 
+@cpu_only
 def test_gqa_validates_like_fwd(L):
     assert fwd_gqa(L, 4, 2, d=96) == UNSUPPORTED
     assert fwd_gqa(L, 4, 2, scale=0.0) == INVALID
@@ -128,6 +143,57 @@ def test_workspace_bytes(L):
     assert L.attn_bwd_workspace_bytes(1, 1, 3, 64, 1) == 2 * 256
     assert L.attn_bwd_workspace_bytes(1, 1, 0, 64, 1) == 0
     assert L.attn_bwd_workspace_bytes(1, 1, 8, 100, 1) == 0
+
+
+def dec(L, fp8=False, ws_bytes=None, **kw):
+    a = dict(q=P, k=P, v=P, ks=P, vs=P, o=P, lse=P, B=2, H=8, H_kv=2, Nq=1, Nk=300, d=128,
+             dtype=1, scale=0.088, causal=1, kv_lens=0, splits=0, ws=P)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = L.attn_decode_workspace_bytes(a["B"], a["H"], a["H_kv"], a["Nq"], a["Nk"],
+                                                 a["d"], a["dtype"], a["splits"])
+    tail = (a["B"], a["H"], a["H_kv"], a["Nq"], a["Nk"], a["d"], a["dtype"], a["scale"],
+            a["causal"], a["kv_lens"], a["splits"], a["ws"], ws_bytes, 0)
+    if fp8:
+        return L.attn_decode_fp8kv(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["o"], a["lse"], *tail)
+    return L.attn_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], *tail)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8kv"])
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=0), INVALID), (dict(k=0), INVALID), (dict(o=0), INVALID), (dict(ws=0), INVALID),
+    (dict(q=P + 8), INVALID), (dict(ws=P + 16), INVALID), (dict(lse=P + 2), INVALID),
+    (dict(kv_lens=P + 1), INVALID), (dict(B=0), INVALID), (dict(Nq=0), INVALID),
+    (dict(Nk=0), INVALID), (dict(H_kv=3), INVALID), (dict(H_kv=0), INVALID),
+    (dict(H_kv=16), INVALID), (dict(splits=-1), INVALID), (dict(dtype=5), INVALID),
+    (dict(dtype=0), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(scale=0.0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(ws_bytes=256), INVALID),
+])
+@cpu_only
+def test_decode_rejects_bad_arguments(L, fp8, kw, want):
+    kw = dict(kw)  # the parameter dict is shared by both formats
+    ws_bytes = kw.pop("ws_bytes", None)
+    assert dec(L, fp8, ws_bytes, **kw) == want
+
+
+@cpu_only
+def test_decode_fp8kv_specific_rules(L):
+    assert dec(L, True, d=64) == UNSUPPORTED   # FP8 caches: d = 128 only
+    assert dec(L, True, ks=0) == INVALID       # both scale arrays are required
+    assert dec(L, True, vs=P + 2) == INVALID
+
+
+def test_decode_workspace_bytes(L):
+    # One split: fp32 O [rows][1][d] and (m, l) [rows][1][2], each section rounded to 256 B.
+    rows = 2 * 8 * 3
+    up = lambda n: (n + 255) // 256 * 256
+    assert L.attn_decode_workspace_bytes(2, 8, 2, 3, 300, 128, 1, 1) == up(rows * 128 * 4) + up(rows * 2 * 4)
+    # More splits never need less; automatic (0) is a valid request; invalid sizes give 0.
+    sizes = [L.attn_decode_workspace_bytes(8, 64, 8, 1, 8192, 128, 1, s) for s in (1, 4, 16, 0)]
+    assert sizes[0] < sizes[1] < sizes[2] and sizes[3] > 0 and all(x % 256 == 0 for x in sizes)
+    assert L.attn_decode_workspace_bytes(1, 4, 3, 1, 100, 128, 1, 0) == 0   # H_kv does not divide H
+    assert L.attn_decode_workspace_bytes(1, 4, 2, 1, 100, 96, 1, 0) == 0    # unsupported d
+    assert L.attn_decode_workspace_bytes(1, 4, 2, 1, 100, 128, 0, 0) == 0   # fp32
 
 
 def test_binding_refuses_cpu_tensors():
