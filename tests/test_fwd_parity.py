@@ -197,6 +197,23 @@ def test_workload_sampled(name):
             assert torch.all(o[b, :, L:] == 0) and torch.all(torch.isneginf(lse[b, :, L:]))
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
+def test_long_context_sampled_rows(causal):
+    """N = 32768 (256 row tiles of 128, 512 key tiles of 64): sampled rows of
+    every head against the oracle, including both ends and tile boundaries."""
+    B, H, N, d = 1, 4, 32768, 128
+    x = make_inputs(B, H, N, d, torch.bfloat16, seed=81 + causal)
+    o, lse = run_fwd(x["q"], x["k"], x["v"], 1 / math.sqrt(d), causal)
+    assert torch.isfinite(o).all()
+    rng = np.random.default_rng(81)
+    for h in range(H):
+        rows = sorted({0, 1, 127, 128, 4095, 16384, N - 65, N - 64, N - 1} |
+                      set(rng.integers(0, N, size=8).tolist()))
+        ro, rl = oracle.attn_ref_rows(x["q"], x["k"], x["v"], 0, h, rows, 1 / math.sqrt(d), causal)
+        assert_close(o[0, h, rows], ro, O_TOL["bf16"], f"N=32768 O (h={h})")
+        assert_close(lse[0, h, rows], rl, LSE_TOL["bf16"], f"N=32768 LSE (h={h})")
+
+
 # ------------------------------------------------------------- edge and stress
 
 @pytest.mark.parametrize("d", [64, 128])
