@@ -15,7 +15,7 @@
 // With S = scale*Q K^T, dQ = scale*dS K and dK = scale*dS^T Q.
 //
 // Three launches on one stream:
-//   bwd_pre:  delta_i = rowsum(dO_i o O_i) and LSE_i*log2(e)    (HBM-bound)
+//   bwd_pre:  -delta_i = -rowsum(dO_i o O_i) and LSE_i*log2(e)  (HBM-bound)
 //   bwd_dkdv: one workgroup per 128 keys; loops over the query tiles that can
 //             see those keys, accumulating dK and dV in registers
 //   bwd_dq:   one workgroup per 128 queries; loops over the key tiles they
@@ -89,8 +89,9 @@ struct TileAddr {
 };
 
 // ---------------------------------------------------------------------------
-// delta_i = sum_d dO_i[d] * O_i[d] in fp32 and lse2_i = LSE_i * log2(e);
-// both 0 for padded rows.
+// delta_i = sum_d dO_i[d] * O_i[d] in fp32, stored negated (the dK/dV kernel
+// starts its dP accumulators at -delta, so dP - delta comes out of the MFMA),
+// and lse2_i = LSE_i * log2(e); both 0 for padded rows.
 // ---------------------------------------------------------------------------
 template <int D, bool F16>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a) {
@@ -115,7 +116,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a) {
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, TPR);
   if (row < total && c == 0) {
-    a.delta[row] = valid ? part : 0.f;
+    a.delta[row] = valid ? -part : 0.f;
     a.lse2[row] = valid ? a.lse[row] * kLog2e : 0.f;
   }
 }
@@ -129,9 +130,18 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a) {
 //   P              = exp2(S*scale*log2e - LSE*log2e), masked
 //   dV^T (d x key) += dO^T P       A = dO^T (transposing LDS read), B = P
 //   dP (q x key)   = dO V^T        A = dO rows (LDS),  B = V (VGPR)
-//   dS             = P o (dP - delta)
+//   dS             = P o (dP - delta)  (dP's accumulator starts at -delta)
 //   dK^T (d x key) += Q^T dS       A = Q^T (transposing LDS read),  B = dS
 // ---------------------------------------------------------------------------
+// Four f32x4 (rows 8g + 4hi + e, as read from the statistics tile) as one
+// accumulator-layout f32x16.
+__device__ __forceinline__ f32x16 join16(const f32x4* x) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = x[i >> 2][i & 3];
+  return r;
+}
+
 template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   constexpr int BN = 128, BM = 64;
@@ -227,8 +237,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     const lds_t* del_t = lse_t + BM * 4;
 
     // Exponentials and dS of sub-block sb; also packs P and dS to bf16.
-    auto softmax_grad = [&](int sb, f32x16& s, f32x16& dp, const f32x4* l4, const f32x4* d4,
-                            e16x8* pb, e16x8* gb) {
+    auto softmax_grad = [&](int sb, f32x16& s, f32x16& dp, const f32x4* l4, e16x8* pb,
+                            e16x8* gb) {
       // Element i is query qt0 + sb*32 + hi*4 + c (c = (i/4)*8 + i%4) against this
       // lane's key; causally visible iff c >= lo.
       const int lo = key - (qt0 + sb * 32) - hi * 4;
@@ -240,7 +250,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
           float p = fast_exp2(fmaf(s[i], c2, -l4[g][e]));
           if (MASKED) p = (g * 8 + e >= lo) ? p : 0.f;
           s[i] = p;
-          dp[i] = p * (dp[i] - d4[g][e]);
+          dp[i] = p * dp[i];  // dp already holds dP - delta
         }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -280,48 +290,49 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     // work of one sub-block runs under the MFMAs of the other and every LDS
     // read is issued a phase ahead of the MFMA that consumes it.
     constexpr int PM = 2 * DS;  // MFMAs per phase
-    // Phase 1a: Q/dO row operands of A.
+    // Phase 1a: statistics and Q/dO row operands of A.
     e16x8 qa[DS], oa[DS];
+    f32x4 lA[4], dA[4];
+    read_stats(0, lA, dA);  // first: -delta_A is the dP_A accumulator's start
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       qa[ds] = ad.rowop(Qt, 0, ds);
       oa[ds] = ad.rowop(dOt, 0, ds);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Phase 1b: S_A = Q_A K^T, dP_A = dO_A V^T; reads: row operands of B, stats of A.
+    // Phase 1b: S_A = Q_A K^T, dP_A = dO_A V^T - delta_A (the accumulator
+    // starts at the rows' -delta); reads: statistics and row operands of B.
     f32x16 sA = mfma32x32x16_z<F16>(qa[0], kreg[0]);
-    f32x16 dpA = mfma32x32x16_z<F16>(oa[0], vreg[0]);
+    f32x16 dpA = mfma32x32x16<F16>(oa[0], vreg[0], join16(dA));
 #pragma unroll
     for (int ds = 1; ds < DS; ++ds) {
       sA = mfma32x32x16<F16>(qa[ds], kreg[ds], sA);
       dpA = mfma32x32x16<F16>(oa[ds], vreg[ds], dpA);
     }
+    f32x4 lB[4], dB[4];
+    read_stats(1, lB, dB);
     e16x8 qb[DS], ob[DS];
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       qb[ds] = ad.rowop(Qt, 32, ds);
       ob[ds] = ad.rowop(dOt, 32, ds);
     }
-    f32x4 lA[4], dA[4];
-    read_stats(0, lA, dA);
 #pragma unroll
     for (int i = 0; i < PM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Phase 2: S_B, dP_B; VALU of A; reads: stats of B, transposed operands of A.
+    // Phase 2: S_B, dP_B - delta_B; VALU of A; reads: transposed operands of A.
     f32x16 sB = mfma32x32x16_z<F16>(qb[0], kreg[0]);
-    f32x16 dpB = mfma32x32x16_z<F16>(ob[0], vreg[0]);
+    f32x16 dpB = mfma32x32x16<F16>(ob[0], vreg[0], join16(dB));
 #pragma unroll
     for (int ds = 1; ds < DS; ++ds) {
       sB = mfma32x32x16<F16>(qb[ds], kreg[ds], sB);
       dpB = mfma32x32x16<F16>(ob[ds], vreg[ds], dpB);
     }
     e16x8 pA[2], gA[2];
-    softmax_grad(0, sA, dpA, lA, dA, pA, gA);
-    f32x4 lB[4], dB[4];
-    read_stats(1, lB, dB);
+    softmax_grad(0, sA, dpA, lA, pA, gA);
     e16x8 trA[2 * DB][2];
     read_tr(0, trA);
 #pragma unroll
@@ -334,7 +345,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     // Phase 3: dV, dK += sub-block A; VALU of B; reads: transposed operands of B.
     grad_mfma(trA, pA, gA);
     e16x8 pB[2], gB[2];
-    softmax_grad(1, sB, dpB, lB, dB, pB, gB);
+    softmax_grad(1, sB, dpB, lB, pB, gB);
     e16x8 trB[2 * DB][2];
     read_tr(1, trB);
 #pragma unroll
@@ -446,7 +457,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
   vdma.load(lds_base(v0_), 0);
 
   const float lse2 = qvalid ? a.lse2[(size_t)bh * N + q] : 0.f;
-  const float dq_delta = qvalid ? a.delta[(size_t)bh * N + q] : 0.f;
+  const float neg_delta = qvalid ? a.delta[(size_t)bh * N + q] : 0.f;  // -delta
   e16x8 qreg[DS], doreg[DS];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds) {
@@ -487,7 +498,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a) {
       for (int i = 0; i < 16; ++i) {
         float p = fast_exp2(fmaf(s[i], c2, -lse2));
         if (MASKED) p = ((i >> 2) * 8 + (i & 3)) <= lim ? p : 0.f;
-        dp[i] = p * (dp[i] - dq_delta);
+        dp[i] = p * (dp[i] + neg_delta);
       }
       gb[0] = pack8<F16>(dp, 0);
       gb[1] = pack8<F16>(dp, 1);

@@ -31,7 +31,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;             // workspace: rowsum(dO o O), fp32 [B,H,N]
+  float* delta;             // workspace: -rowsum(dO o O), fp32 [B,H,N]
   float* lse2;              // workspace: LSE * log2(e), fp32 [B,H,N] (0 on padded rows)
   const int32_t* seqlens;
   int B, H, N;

@@ -115,7 +115,7 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
 
 /*
  * attn_bwd_workspace_bytes - device workspace that attn_bwd needs for these sizes
- * (it holds D_i = rowsum(dO_i o O_i) and LSE_i * log2(e), fp32 [B,H,N] each).
+ * (it holds -D_i = -rowsum(dO_i o O_i) and LSE_i * log2(e), fp32 [B,H,N] each).
  * Returns 0 for invalid sizes.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype dtype);
