@@ -263,7 +263,6 @@ attn_status attn_decode_fp8kv(const void* q, const uint8_t* k8, const uint8_t* v
                               void* workspace, size_t workspace_bytes, attn_stream_t stream) {
   attn_status st = check_decode(B, H, H_kv, Nq, Nk, d, dtype, num_splits);
   if (st != ATTN_OK) return st;
-  if (d != 128) return ATTN_ERR_UNSUPPORTED;
   if (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4))
     return ATTN_ERR_INVALID_ARG;
   return decode_common(q, k8, v8, k_scale, v_scale, o, lse, B, H, H_kv, Nq, Nk, d, dtype, scale,

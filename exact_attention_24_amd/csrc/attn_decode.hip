@@ -352,7 +352,9 @@ hipError_t launch_decode_t(const DecArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_16(const DecArgs& a, int d, bool f16, hipStream_t stream) {
-  if (a.k_scale) {  // FP8 K/V (d = 128 only; checked by the caller)
+  if (a.k_scale) {  // FP8 K/V
+    if (d == 64)
+      return f16 ? launch_decode_t<64, true, true>(a, stream) : launch_decode_t<64, false, true>(a, stream);
     return f16 ? launch_decode_t<128, true, true>(a, stream) : launch_decode_t<128, false, true>(a, stream);
   }
   if (d == 64)

@@ -16,8 +16,10 @@ namespace attn {
 // p ^ swz(r).
 template <int D>
 __device__ __forceinline__ int swz(int r) {
+  static_assert(D == 128 || D == 64 || D == 32, "16 / 8 / 4 chunks per row");
   if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return (r >> 2) & 3;  // 64-byte rows (FP8 rows of 64 elements)
 }
 template <int D>
 __device__ __forceinline__ int tile_off(int r, int chunk) {

@@ -205,8 +205,8 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
  *            are K_j = k8_j * k_scale_j and V_j = v8_j * v_scale_j.
  * q, o, lse, dtype (of q and o), kv_lens, causal, num_splits and the workspace
  * (attn_decode_workspace_bytes with the same arguments) are as for attn_decode.
- * Only d = 128 is implemented (ATTN_ERR_UNSUPPORTED otherwise). HBM carries
- * the 8-bit K/V; each chunk is widened to bf16 on chip (exact), the scales are
+ * d is 64 or 128 as for attn_decode. HBM and LDS carry the 8-bit K/V; each
+ * MFMA operand is widened to the 16-bit format on chip (exact), the scales are
  * applied in fp32 to the scores and to the weights before the V product.
  */
 attn_status attn_decode_fp8kv(const void* q, const uint8_t* k8, const uint8_t* v8,

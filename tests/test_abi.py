@@ -178,7 +178,7 @@ def test_decode_rejects_bad_arguments(L, fp8, kw, want):
 
 @cpu_only
 def test_decode_fp8kv_specific_rules(L):
-    assert dec(L, True, d=64) == UNSUPPORTED   # FP8 caches: d = 128 only
+    assert dec(L, True, d=96) == UNSUPPORTED   # FP8 caches: d = 64 or 128
     assert dec(L, True, ks=0) == INVALID       # both scale arrays are required
     assert dec(L, True, vs=P + 2) == INVALID
 

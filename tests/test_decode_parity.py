@@ -153,7 +153,10 @@ def _fp8_case(x):
     return k8, v8, ks, vs, oracle.dequant_fp8(k8, ks), oracle.dequant_fp8(v8, vs)
 
 
-FP8_SHAPES = [(2, 8, 2, 1, 300), (1, 16, 1, 4, 333), (2, 4, 4, 3, 700), (1, 8, 8, 16, 129)]
+# (B, H, H_kv, Nq, Nk, d)
+FP8_SHAPES = [(2, 8, 2, 1, 300, 128), (1, 16, 1, 4, 333, 128), (2, 4, 4, 3, 700, 128),
+              (1, 8, 8, 16, 129, 128), (2, 8, 2, 1, 300, 64), (1, 16, 1, 4, 333, 64),
+              (2, 4, 4, 3, 700, 64)]
 
 
 @pytest.mark.parametrize("splits", [0, 3])
@@ -164,11 +167,11 @@ def test_decode_fp8kv_small(shape, causal, dtype, splits):
     """FP8 (E4M3, per-token scale) K/V: the oracle attends over the dequantised
     cache in fp64; the bar is the 16-bit path's (the FP8 values are exact on
     chip, the scales are applied in fp32)."""
-    B, H, H_kv, Nq, Nk = shape
-    x = make_inputs(B, H, Nk, 128, dtype, seed=sum(shape) + 5 * causal, H_kv=H_kv, Nq=Nq)
+    B, H, H_kv, Nq, Nk, d = shape
+    x = make_inputs(B, H, Nk, d, dtype, seed=sum(shape) + 5 * causal, H_kv=H_kv, Nq=Nq)
     k8, v8, ks, vs, kd, vd = _fp8_case(x)
-    o, lse = run_decode_fp8(x["q"], k8, v8, ks, vs, 1 / math.sqrt(128), causal, num_splits=splits)
-    ro, rl = oracle.attn_ref_decode(x["q"], kd, vd, 1 / math.sqrt(128), causal)
+    o, lse = run_decode_fp8(x["q"], k8, v8, ks, vs, 1 / math.sqrt(d), causal, num_splits=splits)
+    ro, rl = oracle.attn_ref_decode(x["q"], kd, vd, 1 / math.sqrt(d), causal)
     dn = dtype_name(x["q"])
     assert_close(o, ro, O_TOL[dn], f"fp8 decode{shape} O")
     assert_close(lse, rl, LSE_TOL[dn], f"fp8 decode{shape} LSE")
