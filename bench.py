@@ -17,6 +17,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -124,6 +125,38 @@ def copy_calibration(torch, steps):
     torch.cuda.synchronize()
     print(json.dumps({"mode": "copy", "bytes_read_per_launch": COPY_BYTES,
                       "bytes_written_per_launch": COPY_BYTES, "launches": steps}), flush=True)
+
+
+def gemm_reference(torch, steps, warmup):
+    """A plain bf16 library GEMM (torch.matmul, 8192 x 8192 x 8192) timed the same
+    way as the forward, once on seeded random operands and once on zeros: the
+    dense-MFMA rate a vendor kernel reaches on this GPU under the same power
+    limit, as context for the attention kernel's fraction of the nominal peak."""
+    n = 8192
+    g = torch.Generator("cpu").manual_seed(1234)
+    a = torch.randn(n, n, generator=g).to(torch.bfloat16).to("cuda:0")
+    b = torch.randn(n, n, generator=g).to(torch.bfloat16).to("cuda:0")
+    c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda:0")
+    for kind in ("random", "zeros"):
+        if kind == "zeros":
+            a.zero_()
+            b.zero_()
+        for _ in range(warmup):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, b, out=c)
+            e1.record()
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        med = statistics.median(times)
+        print(json.dumps({"mode": "gemm", "op": "torch.matmul bf16", "M": n, "N": n, "K": n,
+                          "values": kind, "ms_median": round(med, 4),
+                          "tflops": round(2.0 * n ** 3 / med / 1e9, 1)}), flush=True)
 
 
 BWD_WORKLOAD = "causal_fwdbwd_bf16_b2_h16_n8192_d128"
@@ -287,12 +320,14 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=10,
                     help="timed backward passes on the causal B=2 H=16 N=8192 d=128 workload "
                          "(reported under \"bwd\"; 0 skips them)")
-    ap.add_argument("--mode", choices=["fwd", "bwd", "copy", "suite", "decode"], default="fwd",
+    ap.add_argument("--mode", choices=["fwd", "bwd", "copy", "suite", "decode", "gemm"], default="fwd",
                     help="fwd: the benchmark; bwd: the backward alone; suite: forward timings "
                          "of every workload plus a context sweep (one JSON line each); decode: "
                          "the split-KV decode workloads against the HBM roofline; copy: a "
                          "plain device copy of known size, whose FETCH_SIZE/WRITE_SIZE counters "
-                         "calibrate the traffic figure")
+                         "calibrate the traffic figure; gemm: a library bf16 GEMM on random "
+                         "and on zero operands, the dense-MFMA rate reachable under this "
+                         "GPU's power limit (context only)")
     ap.add_argument("--values", choices=["random", "zeros"], default="random",
                     help="fwd mode only: 'zeros' runs the same launches on all-zero Q, K, V, "
                          "a diagnostic of data-dependent power (the clock the chip holds under "
@@ -306,6 +341,9 @@ def main():
     import torch
     if args.mode == "copy":
         copy_calibration(torch, args.steps)
+        return
+    if args.mode == "gemm":
+        gemm_reference(torch, args.steps, args.warmup)
         return
     import exact_attention_24_amd as ea
     if args.mode == "bwd":
