@@ -45,11 +45,10 @@ attn_status check_heads(int H, int H_kv) {
 
 // Split plan of the decode: `splits` key ranges of `chunk_keys` keys (a
 // multiple of 32) per (batch, K/V head). 0 requested splits picks enough for
-// about 768 single-wave workgroups: one resident round at three per CU (the
-// split kernel's 42-48 KiB of LDS) on 256 CUs. More, shorter workgroups were
-// measured slower (each pays its start-up latency again; B=8, 8 K/V heads,
-// 8192 keys: 32 splits 52.7 us, 12 splits 49.6 us for bf16, 53.7 -> 46.9 us
-// for FP8 K/V).
+// one resident round of workgroups on 256 CUs (at most three per CU: the split
+// kernel's 42-48 KiB of LDS). More, shorter workgroups were measured slower
+// (each pays its start-up latency again; B=8, 8 K/V heads, 8192 keys: 32
+// splits 52.7 us, 12 splits 49.6 us for bf16, 53.7 -> 46.9 us for FP8 K/V).
 struct DecodePlan {
   int splits, chunk_keys, col_groups;
 };
