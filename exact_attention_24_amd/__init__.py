@@ -296,6 +296,8 @@ def attn_decode_fp8kv(q, k8, v8, k_scale, v_scale, *, scale: Optional[float] = N
     need = attn_decode_workspace_bytes(B, H, H_kv, Nq, Nk, d, code, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device buffer")
     nbytes = workspace.numel() * workspace.element_size()
     st = lib().attn_decode_fp8kv(q.data_ptr(), k8.data_ptr(), v8.data_ptr(), k_scale.data_ptr(),
                                  v_scale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, H_kv, Nq,
