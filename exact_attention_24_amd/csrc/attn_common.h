@@ -50,6 +50,19 @@ __device__ __forceinline__ f32x16 mfma32x32x16_z(e16x8 a, e16x8 b) {
   return mfma32x32x16<F16>(a, b, z);
 }
 
+// D += A(16x32) * B(32x16), 16-bit inputs, fp32 accumulate. A: lane l holds
+// row l%16, k = 8*(l/16) .. +7.  B: lane l holds column l%16, k = 8*(l/16) ..
+// +7.  D: lane l holds column l%16, rows 4*(l/16) + i, i = 0..3 (layout
+// checked on the device with an in-bounds probe against a host product).
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16x16x32(e16x8 a, e16x8 b, f32x4 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 __device__ __forceinline__ e16x8 as_e16x8(u32x4 v) { return __builtin_bit_cast(e16x8, v); }
@@ -113,6 +126,17 @@ __device__ __forceinline__ float sum_halves(float x) {
   float lo, hi;
   split_halves(x, lo, hi);
   return lo + hi;
+}
+
+// Max / sum over the four lanes l % 16 + {0, 16, 32, 48} (every one of them
+// gets the result).
+__device__ __forceinline__ float max_quarters(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float sum_quarters(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
 }
 
 // ---- 16-bit packing: one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 (round to

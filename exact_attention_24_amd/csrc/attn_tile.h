@@ -25,6 +25,25 @@ template <int D>
 __device__ __forceinline__ int tile_off(int r, int chunk) {
   return r * (D * 2) + ((chunk ^ swz<D>(r)) << 4);
 }
+
+// Two more layouts for 128-column tiles read only by 16x16x32 MFMA operands
+// (both bijections on each row's chunks; measured free of bank conflicts with
+// SQ_LDS_BANK_CONFLICT, where swz above is not for the first pattern):
+//  - TILE_K16, for ds_read_b128 operands that take 16 consecutive rows at 4
+//    consecutive chunks: chunk c of row r at c ^ (r % 16);
+//  - TILE_T16, for transposing reads that take eight consecutive rows at two
+//    consecutive chunks per half-wave: chunk c of row r at c ^ (2 * (r % 8)).
+enum TileLayout { TILE_SWZ = 0, TILE_K16 = 1, TILE_T16 = 2 };
+template <int D, int LAYOUT>
+__device__ __forceinline__ int layout_swz(int r) {
+  if constexpr (LAYOUT == TILE_K16) return r & 15;
+  else if constexpr (LAYOUT == TILE_T16) return 2 * (r & 7);
+  else return swz<D>(r);
+}
+template <int LAYOUT>
+__device__ __forceinline__ int tile_off_128(int r, int col) {
+  return r * 256 + (((col >> 3) ^ layout_swz<128, LAYOUT>(r)) << 4) + ((col >> 2) & 1) * 8;
+}
 // Byte offset of element column `col` (a multiple of 4) of row r.
 template <int D>
 __device__ __forceinline__ int tile_off_col(int r, int col) {
@@ -71,13 +90,15 @@ __device__ __forceinline__ e16x8 pack8(const f32x16& s, int h) {
 // as zeros (hardware range check on the per-lane offset; the scalar offset is
 // left at 0): the tile never holds stale LDS bytes that could be NaN bit
 // patterns, rows past the end are never fetched, and no clamping is needed.
-// NWAVES waves share a tile of ROWS rows; the calling wave fills the 1 KB row
+// LAYOUT selects the chunk layout (swz unless stated). NWAVES waves share a tile of
+// ROWS rows; the calling wave fills the 1 KB row
 // groups g = wave, wave + NWAVES, ... (64/(D/8) rows each), lane l writing
 // physical chunk l % (D/8) of row l / (D/8), i.e. logical chunk
 // (l % (D/8)) ^ swz(row). The per-lane byte offsets do not depend on which
 // tile is loaded, so they are computed once.
-template <int D, int ROWS, int NWAVES>
+template <int D, int ROWS, int NWAVES, int LAYOUT = TILE_SWZ>
 struct TileDma {
+  static_assert(LAYOUT == TILE_SWZ || D == 128, "the 16x16 layouts are for 128-column tiles");
   static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int RPG = 64 / CPR;   // rows per 1 KB wave load
   static constexpr int ITER = ROWS / RPG / NWAVES;
@@ -96,7 +117,7 @@ struct TileDma {
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
       const int r = (wave + it * NWAVES) * RPG + rsub;
-      voff[it] = (uint32_t)(r * D * 2 + ((pc ^ swz<D>(r)) << 4));
+      voff[it] = (uint32_t)(r * D * 2 + ((pc ^ layout_swz<D, LAYOUT>(r)) << 4));
     }
   }
   // Enqueue the loads of rows [row0, row0 + ROWS) into `tile`.
