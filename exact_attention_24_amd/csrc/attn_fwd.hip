@@ -28,35 +28,42 @@ namespace {
 
 // ----------------------------------------------------------------------------
 // 16-bit inputs (bf16, or fp16 with F16), MFMA products, fp32 softmax and
-// accumulation. This body (32x32x16 MFMAs) runs d = 64; d = 128 runs the
-// 16x16x32 body further down, which follows the same scheme.
+// accumulation.
 //
 // Workgroup: 4 waves, 128 query rows (32 per wave), K/V tiles of 64 keys,
 // double-buffered in LDS and filled by direct global->LDS loads
 // (global_load_lds_dwordx4, no VGPR staging). Scores are computed transposed,
-// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (_f16): K (from LDS) is the A
-// operand and Q (held in VGPRs for the whole loop) is the B operand, so each
-// lane's accumulator holds keys of ONE query. Row reductions (sum, and the max
-// where one is taken) are in-lane operations plus one exchange between the two
-// 32-lane halves. The output is
-// accumulated transposed as well, O^T += V^T P^T: P^T stays in the lanes it was
-// computed in (B operand) and V^T is read from the row-major V tile with the
-// transposing LDS load, in the key order P^T's lanes hold.
+// S^T = K Q^T, from v_mfma_f32_16x16x32_bf16 (_f16) blocks: K (from LDS) is
+// the A operand and Q (held in VGPRs for the whole loop) the B operand. Lane
+// l (c = l % 16, g = l / 16) holds the queries qw + c and qw + 16 + c, each
+// with the keys 16*kb + 4*g + i of the tile (kb, i = 0..3), so one query's 64
+// keys lie in the lanes c, c+16, c+32, c+48. Each K operand read feeds both
+// 16-query blocks, which keeps the LDS bytes per FLOP of 32x32x16 blocks,
+// while the 16x16 shape holds a higher clock under the GPU's power limit
+// (measured ~1.93 against ~1.76 GHz for the same kernel on 32x32x16 blocks at
+// d = 128, +5% net). The output is accumulated transposed as well,
+// O^T += V^T P^T: the MFMA k index 8g + e stands for key 32jj + 4g + e (e < 4)
+// or 32jj + 16 + 4g + e - 4, the order in which the score accumulators already
+// hold P^T, so the weights are packed in place as B operands, and V^T is read
+// from the row-major V tile with the transposing LDS load in that key order.
+// K and V tiles use the TILE_K16 and TILE_T16 layouts, in which these reads
+// are free of bank conflicts.
 //
 // Softmax arithmetic per score: one FMA (s*scale*log2e - m*scale*log2e), one
-// v_exp_f32 (exp2), one fp32 add into the row sum and a share of a bf16 pack;
-// statistics stay in fp32 and only the P V product sees bf16 weights. The
-// rescale of [SafeSoftmax] §3.2 is applied lazily against a reference max m:
-// the first tile sets m to its exact row max, and later tiles are weighted
-// against m without taking their own max. A weight can exceed 2^8 only if
-// its lane's partial row sum does, so that sum (which is needed anyway) is
-// the check; when it fails (rare: a score more than 8/(scale*log2e) above the
-// reference) the tile's scores are recomputed, m moves to the exact max, and
-// O and l are rescaled. Weights stay <= 256, far from fp32 or bf16 range
-// limits, and O / l and LSE use the same reference, so the result is the same
-// softmax. The P V phase runs at raised wave priority (s_setprio): with two
-// waves per SIMD (one from each resident workgroup), the wave holding P V
-// MFMAs is issued first when both are ready (measured 2-4% faster).
+// v_exp_f32 (exp2), one fp32 add into the lane's partial row sum and a share
+// of a 16-bit pack; statistics stay in fp32 and only the P V product sees
+// 16-bit weights. The rescale of [SafeSoftmax] §3.2 is applied lazily against
+// a reference max m: the first tile sets m to its exact row max (the only
+// per-tile use of the two lane exchanges), and later tiles are weighted
+// against m without taking their own max. A weight can exceed 2^8 only if its
+// lane's partial row sum does, so that sum (needed anyway) is the check; when
+// it fails (rare: a score more than 8/(scale*log2e) above the reference) the
+// tile's scores are recomputed, m moves to the exact max, and O and l are
+// rescaled. Weights stay <= 256, far from fp32 or bf16 range limits, and O / l
+// and LSE use the same reference, so the result is the same softmax. The P V
+// phase runs at raised wave priority (s_setprio): with two waves per SIMD (one
+// from each resident workgroup), the wave holding P V MFMAs is issued first
+// when both are ready (measured 2-4% faster).
 // ----------------------------------------------------------------------------
 constexpr float kLazyRescaleW = 256.0f;  // largest unnormalised weight kept without rescaling
 
@@ -80,233 +87,8 @@ template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void fwd_16_body(const FwdArgs& a) {
   constexpr int BM = 128, BN = 64;
   constexpr int TILE = BN * D * 2;
-  constexpr int CH = D / 8;           // 16-byte chunks per row
-  constexpr int DS = D / 16, DB = D / 32;
-
-  // One LDS array per (stage, tensor): distinct objects let the compiler see
-  // that reads of one stage never alias the direct-to-LDS loads filling the
-  // other, so it does not stall them on the prefetch (with a single array it
-  // waited for the next tile's loads before every transposed V read).
-  __shared__ __attribute__((aligned(1024))) char k0_[TILE], v0_[TILE], k1_[TILE], v1_[TILE];
-  lds_t* const kst[2] = {lds_base(k0_), lds_base(k1_)};
-  lds_t* const vst[2] = {lds_base(v0_), lds_base(v1_)};
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int N = a.N;
-  const int nm = (N + BM - 1) / BM;
-  int bh, mt;
-  const int group = a.H / a.H_kv;
-  if (a.seqlens && a.B <= 64 && ((a.H / group) & 7) == 0) {
-    int rank, h;
-    varlen_order(blockIdx.x, nm, a.H, group, CAUSAL, rank, h, mt);
-    bh = batch_of_rank(a.seqlens, a.B, N, rank) * a.H + h;
-  } else {
-    tile_order(blockIdx.x, nm, a.B * a.H, group, CAUSAL, bh, mt);
-  }
-  const int b = bh / a.H;
-  int L = N;
-  if (a.seqlens) L = min(max(a.seqlens[b], 0), N);
-  const int m0 = mt * BM;
-  const size_t hoff = (size_t)bh * N * D;
-  // Grouped K/V heads: query head h reads K/V head h / (H / H_kv).
-  const size_t kvoff = (size_t)(b * a.H_kv + (bh % a.H) / (a.H / a.H_kv)) * N * D;
-  const e16_t* __restrict__ Qh = (const e16_t*)a.q + hoff;
-  e16_t* __restrict__ Oh = (e16_t*)a.o + hoff;
-  float* __restrict__ lse_h = a.lse ? a.lse + (size_t)bh * N : nullptr;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-
-  if (m0 >= L) {  // the whole row tile is padding: O = 0, LSE = -inf
-    const int rows = min(BM, N - m0);
-    for (int c = tid; c < rows * CH; c += 256)
-      gstore16(Oh + (size_t)(m0 + c / CH) * D + (c % CH) * 8, zero4);
-    if (lse_h)
-      for (int r = tid; r < rows; r += 256) lse_h[m0 + r] = -INFINITY;
-    return;
-  }
-
-  const int kv_end = CAUSAL ? min(L, m0 + BM) : L;
-  const int nt = (kv_end + BN - 1) / BN;                 // tiles the workgroup loads
-  const int qw = m0 + wave * 32;                         // first query row of this wave
-  const int q = qw + l32;                                // this lane's query row
-  const int w_end = (qw >= L) ? 0 : (CAUSAL ? min(L, qw + 32) : L);
-  const int wnt = (w_end + BN - 1) / BN;                 // tiles this wave computes
-
-  // K/V rows at or past L are never fetched (the DMA reads zeros there), so
-  // whatever the padding holds cannot reach a valid row through 0 * x.
-  const TileDma<D, BN, 4> kdma((const e16_t*)a.k + kvoff, L, wave, lane);
-  const TileDma<D, BN, 4> vdma((const e16_t*)a.v + kvoff, L, wave, lane);
-  kdma.load(kst[0], 0);
-  vdma.load(vst[0], 0);
-
-  // Q rows -> VGPRs, B-operand layout: lane holds query q, d = 16*ds + 8*hi .. +7.
-  e16x8 qr[DS];
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds)
-    qr[ds] = as_e16x8(q < L ? gload16(Qh + (size_t)q * D + ds * 16 + hi * 8) : zero4);
-
-  f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m_ref = kMaxInit, l_part = 0.f;
-  const float c2 = a.scale_log2;
-
-  // One KV tile: j is the tile index, ST the LDS stage it is in. The two calls
-  // below pass literal stages and are inlined, so every LDS address is a
-  // loop-invariant register plus an immediate offset.
-  auto tile_step = [&](int j, const int ST) {
-    const int n0 = j * BN;
-    if (j + 1 < nt) {
-      kdma.load(kst[ST ^ 1], n0 + BN);
-      vdma.load(vst[ST ^ 1], n0 + BN);
-    }
-    if (j < wnt) {
-      const lds_t* kt = kst[ST];
-      const lds_t* vt = vst[ST];
-      f32x16 s0, s1;
-      // S^T (64 keys x 32 queries) as two 32x32 blocks, masked.
-      auto scores = [&]() {
-        s0 = mfma32x32x16_z<F16>(row_operand<D>(kt, 0, 0, lane), qr[0]);
-        s1 = mfma32x32x16_z<F16>(row_operand<D>(kt, 32, 0, lane), qr[0]);
-#pragma unroll
-        for (int ds = 1; ds < DS; ++ds) {
-          s0 = mfma32x32x16<F16>(row_operand<D>(kt, 0, ds * 2, lane), qr[ds], s0);
-          s1 = mfma32x32x16<F16>(row_operand<D>(kt, 32, ds * 2, lane), qr[ds], s1);
-        }
-        // Keep several K operand reads in flight ahead of the score MFMAs.
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * DS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i < 2 * DS - 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        // Key n0 + hi*4 + c (c = (i/4)*8 + i%4, +32 for s1) is visible iff c <= lim.
-        if (n0 + BN > L || (CAUSAL && n0 + BN - 1 > qw)) {
-          const int lim = (CAUSAL ? min(q, L - 1) : L - 1) - n0 - hi * 4;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int c = (i >> 2) * 8 + (i & 3);
-            s0[i] = c <= lim ? s0[i] : -INFINITY;
-            s1[i] = c + 32 <= lim ? s1[i] : -INFINITY;
-          }
-        }
-      };
-      auto tile_max = [&]() {
-        float mx = max3f(s0[0], s0[1], s1[0]);
-        mx = max3f(mx, s1[1], s0[2]);
-#pragma unroll
-        for (int i = 2; i < 15; ++i) mx = max3f(mx, s1[i], s0[i + 1]);
-        return max_halves(fmaxf(mx, s1[15]));
-      };
-      float sa, sb;
-      auto weights = [&]() {
-        const float mc = m_ref * c2;
-        sa = 0.f;
-        sb = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s0[i] = fast_exp2(fmaf(s0[i], c2, -mc));
-          s1[i] = fast_exp2(fmaf(s1[i], c2, -mc));
-          sa += s0[i];
-          sb += s1[i];
-        }
-      };
-      scores();
-      // The first tile sets the reference max (every lane sees at least one
-      // key of it; O and l are still zero, so nothing is rescaled).
-      if (j == 0) m_ref = tile_max();
-      weights();
-      // A weight above 2^8 means the reference is stale: every weight is at
-      // most its lane's partial row sum, so the check needs no max. Rare:
-      // recompute the scores, move the reference to the exact max, rescale.
-      if (__builtin_amdgcn_ballot_w64(!(sa + sb <= kLazyRescaleW))) {
-        scores();
-        const float m_new = fmaxf(m_ref, tile_max());
-        const float alpha = fast_exp2((m_ref - m_new) * c2);
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-        m_ref = m_new;
-        weights();
-      }
-      l_part += sa + sb;
-      // P^T -> bf16 B operands, one per 16-key step.
-      const e16x8 pb[4] = {pack8<F16>(s0, 0), pack8<F16>(s0, 1), pack8<F16>(s1, 0), pack8<F16>(s1, 1)};
-      __builtin_amdgcn_s_setprio(1);
-      // O^T (D x 32) += V^T (D x 64) P^T (64 x 32).
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          o[db] = mfma32x32x16<F16>(tr_operand<D>(vt, ks * 16, db * 32, lane), pb[ks], o[db]);
-      // Transposed V reads: eight in flight ahead of the P V MFMAs.
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-#pragma unroll
-      for (int i = 0; i < 4 * DB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (i < 4 * DB - 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    dma_wait();
-    __syncthreads();
-  };
-
-  dma_wait();
-  __syncthreads();
-  for (int j = 0; j < nt; j += 2) {
-    tile_step(j, 0);
-    if (j + 1 < nt) tile_step(j + 1, 1);
-  }
-
-  // Epilogue: O = O_acc / l, rounded to bf16; LSE = m*scale + ln l.
-  const float l_tot = sum_halves(l_part);
-  const bool valid = q < L && l_tot > 0.f;
-  const float inv = valid ? 1.f / l_tot : 0.f;
-  if (q < N) {
-    e16_t* orow = Oh + (size_t)q * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = {pack2<F16>(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
-                         pack2<F16>(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-        gstore8(orow + db * 32 + g * 8 + hi * 4, w);
-      }
-    if (lse_h && hi == 0) lse_h[q] = valid ? m_ref * a.scale + logf(l_tot) : -INFINITY;
-  }
-}
-
-// ----------------------------------------------------------------------------
-// d = 128: the same workgroup, tiles, masks and online softmax as above, with
-// the two products built from v_mfma_f32_16x16x32 blocks. Under the GPU's
-// power limit this shape runs at a higher clock for the same work (measured
-// ~1.93 vs ~1.76 GHz on this kernel, +5% net), and each LDS operand still
-// feeds two MFMAs (the wave's two 16-query blocks), so the LDS bytes per FLOP
-// are unchanged.
-//
-// Lane l: c = l % 16, g = l / 16. The scores S^T (64 keys x 32 queries) are
-// 4 key blocks kb x 2 query blocks qb: lane l holds query qw + 16*qb + c and
-// keys 16*kb + 4*g + i (i = 0..3). One query's 64 keys lie in the four lanes
-// c, c+16, c+32, c+48, so its row max and sum take two exchanges; they are
-// needed only for the first tile, a rescale and the epilogue, since the lazy
-// rescale check uses each lane's partial sum (a weight above 2^8 makes that
-// partial sum exceed it). For P V the MFMA k index 8g + e stands for key
-// 32jj + 4g + e (e < 4) or 32jj + 16 + 4g + e - 4: the order in which the
-// score accumulators already hold P^T, so the weights need no exchange, and
-// the V^T operand is read in that key order by the transposing LDS load. K and
-// V tiles use the TILE_K16 and TILE_T16 layouts, conflict-free for these reads.
-// ----------------------------------------------------------------------------
-template <bool CAUSAL, bool F16>
-__device__ __forceinline__ void fwd_16x16_body(const FwdArgs& a) {
-  constexpr int D = 128, BM = 128, BN = 64;
-  constexpr int TILE = BN * D * 2;
   constexpr int CH = D / 8;
+  constexpr int DC = D / 32, DBK = D / 16;  // 32-wide d chunks (Q, K), 16-wide d blocks (O, V)
 
   __shared__ __attribute__((aligned(1024))) char k0_[TILE], v0_[TILE], k1_[TILE], v1_[TILE];
   lds_t* const kst[2] = {lds_base(k0_), lds_base(k1_)};
@@ -360,27 +142,27 @@ __device__ __forceinline__ void fwd_16x16_body(const FwdArgs& a) {
   vdma.load(vst[0], 0);
 
   // Q as B operands: query qq[qb], d = 32*dc + 8*g .. +7.
-  e16x8 qr[2][4];
+  e16x8 qr[2][DC];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc)
+    for (int dc = 0; dc < DC; ++dc)
       qr[qb][dc] = as_e16x8(qq[qb] < L ? gload16(Qh + (size_t)qq[qb] * D + dc * 32 + g * 8) : zero4);
 
   // Per-lane LDS offsets. K operand: key 16*kb + c, columns 32*dc + 8*g .. +7.
   // V^T operand: row 4*g + c/4 (+16 for the upper half), columns
   // 16*db + 4*(c%4) .. +3. Offsets of whole 16-row blocks leave both swizzles
   // unchanged and become immediates.
-  uint32_t koff[4], voff[8];
+  uint32_t koff[DC], voff[DBK];
 #pragma unroll
-  for (int dc = 0; dc < 4; ++dc) koff[dc] = (uint32_t)tile_off_128<TILE_K16>(c16, dc * 32 + g * 8);
+  for (int dc = 0; dc < DC; ++dc) koff[dc] = (uint32_t)tile_off_lay<D, TILE_K16>(c16, dc * 32 + g * 8);
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
-    voff[db] = (uint32_t)tile_off_128<TILE_T16>(4 * g + (c16 >> 2), db * 16 + 4 * (c16 & 3));
+  for (int db = 0; db < DBK; ++db)
+    voff[db] = (uint32_t)tile_off_lay<D, TILE_T16>(4 * g + (c16 >> 2), db * 16 + 4 * (c16 & 3));
 
-  f32x4 o[8][2];  // O^T block (d 16*db + 4*g + i, query qq[qb])
+  f32x4 o[DBK][2];  // O^T block (d 16*db + 4*g + i, query qq[qb])
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < DBK; ++db)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -401,7 +183,7 @@ __device__ __forceinline__ void fwd_16x16_body(const FwdArgs& a) {
       // S^T blocks, masked; each K operand read feeds both query blocks.
       auto scores = [&]() {
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc)
+        for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
             const e16x8 kop = as_e16x8(lds_load16(kt + kb * 16 * (D * 2) + koff[dc]));
@@ -413,9 +195,9 @@ __device__ __forceinline__ void fwd_16x16_body(const FwdArgs& a) {
           }
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 4 * DC; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (i < 4 * DC - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         // Key n0 + 16*kb + 4*g + i is visible iff 16*kb + i <= lim.
         if (n0 + BN > L || (CAUSAL && n0 + BN - 1 > qw)) {
@@ -467,7 +249,7 @@ __device__ __forceinline__ void fwd_16x16_body(const FwdArgs& a) {
           const float alpha = fast_exp2((m_ref[qb] - m_new) * c2);
           l_part[qb] *= alpha;
 #pragma unroll
-          for (int db = 0; db < 8; ++db)
+          for (int db = 0; db < DBK; ++db)
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[db][qb][i] *= alpha;
           m_ref[qb] = m_new;
@@ -494,7 +276,7 @@ __device__ __forceinline__ void fwd_16x16_body(const FwdArgs& a) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
+        for (int db = 0; db < DBK; ++db) {
           const lds_t* p = vt + jj * 32 * (D * 2) + voff[db];
           const e16x8 vop = join_e16x8(lds_load_tr16(p), lds_load_tr16(p + 16 * (D * 2)));
 #pragma unroll
@@ -502,9 +284,9 @@ __device__ __forceinline__ void fwd_16x16_body(const FwdArgs& a) {
         }
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
+      for (int i = 0; i < 4 * DBK; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (i < 26) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        if (i < 4 * DBK - 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -529,7 +311,7 @@ __device__ __forceinline__ void fwd_16x16_body(const FwdArgs& a) {
     if (q < N) {
       e16_t* orow = Oh + (size_t)q * D;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < DBK; ++db) {
         const u32x2 w = {pack2<F16>(o[db][qb][0] * inv, o[db][qb][1] * inv),
                          pack2<F16>(o[db][qb][2] * inv, o[db][qb][3] * inv)};
         gstore8(orow + db * 16 + 4 * g, w);
@@ -545,8 +327,7 @@ __device__ __forceinline__ void fwd_16x16_body(const FwdArgs& a) {
 // dropped some of them).
 template <int D, bool CAUSAL, bool F16>
 __global__ void __launch_bounds__(256, 2) fwd_16_kernel(FwdArgs a) {
-  if constexpr (D == 128) fwd_16x16_body<CAUSAL, F16>(a);
-  else fwd_16_body<D, CAUSAL, F16>(a);
+  fwd_16_body<D, CAUSAL, F16>(a);
 }
 
 // ----------------------------------------------------------------------------

@@ -36,13 +36,14 @@ __device__ __forceinline__ int tile_off(int r, int chunk) {
 enum TileLayout { TILE_SWZ = 0, TILE_K16 = 1, TILE_T16 = 2 };
 template <int D, int LAYOUT>
 __device__ __forceinline__ int layout_swz(int r) {
-  if constexpr (LAYOUT == TILE_K16) return r & 15;
-  else if constexpr (LAYOUT == TILE_T16) return 2 * (r & 7);
+  if constexpr (LAYOUT == TILE_K16) return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  else if constexpr (LAYOUT == TILE_T16) return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
   else return swz<D>(r);
 }
-template <int LAYOUT>
-__device__ __forceinline__ int tile_off_128(int r, int col) {
-  return r * 256 + (((col >> 3) ^ layout_swz<128, LAYOUT>(r)) << 4) + ((col >> 2) & 1) * 8;
+// Byte offset of element column `col` (a multiple of 4) of row r.
+template <int D, int LAYOUT>
+__device__ __forceinline__ int tile_off_lay(int r, int col) {
+  return r * (D * 2) + (((col >> 3) ^ layout_swz<D, LAYOUT>(r)) << 4) + ((col >> 2) & 1) * 8;
 }
 // Byte offset of element column `col` (a multiple of 4) of row r.
 template <int D>
@@ -98,7 +99,7 @@ __device__ __forceinline__ e16x8 pack8(const f32x16& s, int h) {
 // tile is loaded, so they are computed once.
 template <int D, int ROWS, int NWAVES, int LAYOUT = TILE_SWZ>
 struct TileDma {
-  static_assert(LAYOUT == TILE_SWZ || D == 128, "the 16x16 layouts are for 128-column tiles");
+  static_assert(LAYOUT == TILE_SWZ || D == 128 || D == 64, "16x16 layouts: 64 or 128 columns");
   static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int RPG = 64 / CPR;   // rows per 1 KB wave load
   static constexpr int ITER = ROWS / RPG / NWAVES;
