@@ -39,55 +39,6 @@ __device__ __forceinline__ int seq_len(const BwdArgs& a, int b) {
   return a.seqlens ? min(max(a.seqlens[b], 0), a.N) : a.N;
 }
 
-// Store a transposed 32-row accumulator block: lane holds column `row` of the
-// result and values for d = db*32 + g*8 + hi*4 + {0..3}. A lane with
-// valid == false stores zeros (selected, so a non-finite accumulator in a
-// discarded lane cannot leak through a multiply by 0).
-template <int DB, bool F16>
-__device__ __forceinline__ void store_rowT(e16_t* rowp, const f32x16* acc, float mul, bool valid,
-                                           int hi) {
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t w0 = pack2<F16>(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul);
-      const uint32_t w1 = pack2<F16>(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
-      const u32x2 w = {valid ? w0 : 0u, valid ? w1 : 0u};
-      gstore8(rowp + db * 32 + g * 8 + hi * 4, w);
-    }
-}
-
-// Per-lane LDS byte offsets of the MFMA operands of a swizzled [rows][D] tile,
-// computed once per kernel (the swizzle depends on the row modulo 16 only):
-//   row[ds]    A operand, row lane%32 (+ row0, a multiple of 32), chunk 2ds + lane/32
-//   tr[db][h]  transposed operand (see tr_operand) at column db*32, rows
-//              8h + 4*(lane/32) + (lane&15)/4 (+ row0, a multiple of 16)
-template <int D>
-struct TileAddr {
-  static constexpr int DS = D / 16, DB = D / 32;
-  int row[DS];
-  int tr[DB][2];
-  __device__ __forceinline__ explicit TileAddr(int lane) {
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) row[ds] = tile_off<D>(lane & 31, ds * 2 + (lane >> 5));
-    const int r = (lane >> 5) * 4 + ((lane & 15) >> 2);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int col = db * 32 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-      tr[db][0] = tile_off_col<D>(r, col);
-      tr[db][1] = tile_off_col<D>(r + 8, col);
-    }
-  }
-  __device__ __forceinline__ e16x8 rowop(const lds_t* t, int row0, int ds) const {
-    return as_e16x8(lds_load16(t + row[ds] + row0 * (D * 2)));
-  }
-  __device__ __forceinline__ e16x8 trop(const lds_t* t, int row0, int db) const {
-    const u32x2 lo = lds_load_tr16(t + tr[db][0] + row0 * (D * 2));
-    const u32x2 up = lds_load_tr16(t + tr[db][1] + row0 * (D * 2));
-    return join_e16x8(lo, up);
-  }
-};
-
 // ---------------------------------------------------------------------------
 // delta_i = sum_d dO_i[d] * O_i[d] in fp32, stored negated (the dK/dV kernel
 // starts its dP accumulators at -delta, so dP - delta comes out of the MFMA),
@@ -132,34 +83,32 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a) {
 //   dP (q x key)   = dO V^T        A = dO rows (LDS),  B = V (VGPR)
 //   dS             = P o (dP - delta)  (dP's accumulator starts at -delta)
 //   dK^T (d x key) += Q^T dS       A = Q^T (transposing LDS read),  B = dS
+// The products are built from v_mfma_f32_16x16x32 blocks (as in the forward,
+// for the clock the power limit allows; measured 6% faster for this kernel
+// than 32x32x16 blocks). Lane l: c = l % 16, g = l / 16, keys kw + c and
+// kw + 16 + c. The score accumulators hold queries 16*qb + 4*g + i of a
+// sub-block, so one 16-byte read of the statistics tile gives a lane its four
+// rows' LSE or delta (the latter is the dP accumulator's start). For the dV
+// and dK products the MFMA k index 8g + e stands for query 4g + e (e < 4) or
+// 16 + 4g + e - 4 of the sub-block, so P and dS are packed in place and dO^T,
+// Q^T are read in that order. Q and dO tiles, read both ways, use the
+// TILE_T16 layout.
 // ---------------------------------------------------------------------------
-// Four f32x4 (rows 8g + 4hi + e, as read from the statistics tile) as one
-// accumulator-layout f32x16.
-__device__ __forceinline__ f32x16 join16(const f32x4* x) {
-  f32x16 r;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) r[i] = x[i >> 2][i & 3];
-  return r;
-}
-
 template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   constexpr int BN = 128, BM = 64;
   constexpr int TILE = BM * D * 2;
   constexpr int CH = D / 8;
-  constexpr int DS = D / 16, DB = D / 32;
+  constexpr int DC = D / 32, DBK = D / 16;
 
   __shared__ __attribute__((aligned(1024))) char q0_[TILE], q1_[TILE], o0_[TILE], o1_[TILE];
   __shared__ __attribute__((aligned(256))) char st0_[2 * BM * 4], st1_[2 * BM * 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
+  const int c16 = lane & 15, g = lane >> 4;
   const int N = a.N;
   const int nkt = (N + BN - 1) / BN;
-  // One workgroup per (batch, K/V head, key tile); with grouped K/V heads its
-  // dK, dV sum the contributions of the G = H / H_kv query heads that read
-  // this K/V head (query head h reads K/V head h / G).
   int bkv, kt;
   tile_order(blockIdx.x, nkt, a.B * a.H_kv, 1, false, bkv, kt);
   const int b = bkv / a.H_kv, G = a.H / a.H_kv;
@@ -183,22 +132,16 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     return;
   }
 
-  const int kw = n0 + wave * 32;  // first key of this wave
-  const int key = kw + l32;       // this lane's key (B-operand column)
+  const int kw = n0 + wave * 32;                    // first key of this wave
+  const int keys[2] = {kw + c16, kw + 16 + c16};    // this lane's keys (kb = 0, 1)
   const int q_begin = CAUSAL ? (n0 / BM) * BM : 0;
-  // Query tiles are taken in pairs (one per LDS stage); an odd count gets one
-  // more tile past L, which loads as zeros and is fully masked.
   const int nqt = ((L - q_begin + BM - 1) / BM + 1) & ~1;
   const float c2 = a.scale_log2;
 
-  // Per query head of the group (set in the head loop below).
-  TileDma<D, BM, 4> qdma((const e16_t*)a.q, L, wave, lane);
-  TileDma<D, BM, 4> odma((const e16_t*)a.dO, L, wave, lane);
+  TileDma<D, BM, 4, TILE_T16> qdma((const e16_t*)a.q, L, wave, lane);
+  TileDma<D, BM, 4, TILE_T16> odma((const e16_t*)a.dO, L, wave, lane);
   const float* lse2_h = a.lse2;
   const float* delta_h = a.delta;
-  // Stage st: Q tile, dO tile, then lse2[BM] and delta[BM] of the same rows.
-  // Waves 0 and 2 both fetch lse2 and waves 1 and 3 both fetch delta (the
-  // same bytes to the same place), which keeps the code free of branches.
   auto load_tile = [&](int q0, int st) {
     qdma.load(lds_base(st ? q1_ : q0_), q0);
     odma.load(lds_base(st ? o1_ : o0_), q0);
@@ -206,28 +149,34 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     vec64_dma(lds_base(st ? st1_ : st0_) + odd * (BM * 4), odd ? delta_h : lse2_h, L, q0, lane);
   };
 
-  e16x8 kreg[DS], vreg[DS];
+  // K^T, V^T as B operands: key keys[kb], d = 32*dc + 8*g .. +7.
+  e16x8 kreg[2][DC], vreg[2][DC];
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds) {
-    const size_t off = (size_t)key * D + ds * 16 + hi * 8;
-    kreg[ds] = as_e16x8(key < L ? gload16(Kh + off) : zero4);
-    vreg[ds] = as_e16x8(key < L ? gload16(Vh + off) : zero4);
-  }
-  const TileAddr<D> ad(lane);
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const size_t off = (size_t)keys[kb] * D + dc * 32 + g * 8;
+      kreg[kb][dc] = as_e16x8(keys[kb] < L ? gload16(Kh + off) : zero4);
+      vreg[kb][dc] = as_e16x8(keys[kb] < L ? gload16(Vh + off) : zero4);
+    }
+  // LDS offsets: row operands (query 16*qb + c, columns 32*dc + 8*g ..) and
+  // transposed operands (rows 4*g + c/4 (+16), columns 16*db + 4*(c%4) ..);
+  // whole 16-row blocks leave the layout unchanged.
+  uint32_t roff[DC], toff[DBK];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) roff[dc] = (uint32_t)tile_off_lay<D, TILE_T16>(c16, dc * 32 + g * 8);
+#pragma unroll
+  for (int db = 0; db < DBK; ++db)
+    toff[db] = (uint32_t)tile_off_lay<D, TILE_T16>(4 * g + (c16 >> 2), db * 16 + 4 * (c16 & 3));
 
-  f32x16 dk[DB], dv[DB];
+  f32x4 dk[DBK][2], dv[DBK][2];  // dK^T, dV^T blocks (d 16*db + 4*g + i, key keys[kb])
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DBK; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { dk[db][i] = 0.f; dv[db][i] = 0.f; }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { dk[db][kb][i] = 0.f; dv[db][kb][i] = 0.f; }
 
-  // MASKED is set for the two tiles on the causal diagonal only. Elsewhere no
-  // mask is needed: every key of the tile is visible to every query, and rows
-  // at or past L hold zeros (Q, dO, delta, lse2 all 0, so p = 1 and dS = 0)
-  // and add nothing to dK or dV; lanes whose key is at or past L are
-  // discarded at the store.
-  // The next tile's loads are issued first (past the end they read zeros and
-  // touch no memory), so the tile body is a single basic block.
   auto step = [&](int t, const int st, const bool MASKED) {
     const int qt0 = q_begin + t * BM;
     load_tile(qt0 + BM, st ^ 1);
@@ -236,52 +185,79 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     const lds_t* lse_t = lds_base(st ? st1_ : st0_);
     const lds_t* del_t = lse_t + BM * 4;
 
-    // Exponentials and dS of sub-block sb; also packs P and dS to bf16.
-    auto softmax_grad = [&](int sb, f32x16& s, f32x16& dp, const f32x4* l4, e16x8* pb,
-                            e16x8* gb) {
-      // Element i is query qt0 + sb*32 + hi*4 + c (c = (i/4)*8 + i%4) against this
-      // lane's key; causally visible iff c >= lo.
-      const int lo = key - (qt0 + sb * 32) - hi * 4;
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
-          float p = fast_exp2(fmaf(s[i], c2, -l4[g][e]));
-          if (MASKED) p = (g * 8 + e >= lo) ? p : 0.f;
-          s[i] = p;
-          dp[i] = p * dp[i];  // dp already holds dP - delta
-        }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        pb[h] = pack8<F16>(s, h);
-        gb[h] = pack8<F16>(dp, h);
-      }
-    };
+    // Sub-block sb: queries qt0 + 32*sb + 16*qb + 4*g + i in the accumulators.
     auto read_stats = [&](int sb, f32x4* l4, f32x4* d4) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int rl = sb * 32 + g * 8 + hi * 4;  // first of 4 consecutive query rows
-        l4[g] = *(const ATTN_LDS f32x4*)(lse_t + rl * 4);
-        d4[g] = *(const ATTN_LDS f32x4*)(del_t + rl * 4);
+      for (int qb = 0; qb < 2; ++qb) {
+        const int rl = sb * 32 + qb * 16 + g * 4;
+        l4[qb] = *(const ATTN_LDS f32x4*)(lse_t + rl * 4);
+        d4[qb] = *(const ATTN_LDS f32x4*)(del_t + rl * 4);
       }
     };
-    auto read_tr = [&](int sb, e16x8 (*qo)[2]) {  // qo[h*DB + db] = {dO^T, Q^T}
+    auto read_rows = [&](int sb, e16x8 (*qo)[DC][2]) {  // qo[qb][dc] = {Q, dO}
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          qo[h * DB + db][0] = ad.trop(dOt, sb * 32 + h * 16, db);
-          qo[h * DB + db][1] = ad.trop(Qt, sb * 32 + h * 16, db);
+        for (int dc = 0; dc < DC; ++dc) {
+          const int r0 = (sb * 32 + qb * 16) * (D * 2);
+          qo[qb][dc][0] = as_e16x8(lds_load16(Qt + r0 + roff[dc]));
+          qo[qb][dc][1] = as_e16x8(lds_load16(dOt + r0 + roff[dc]));
         }
+    };
+    // S = Q K^T and dP - delta = dO V^T - delta (the accumulator starts at -delta).
+    auto scores = [&](e16x8 (*qo)[DC][2], const f32x4* d4, f32x4 (*s)[2], f32x4 (*dp)[2]) {
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            s[qb][kb] = mfma16x16x32<F16>(qo[qb][dc][0], kreg[kb][dc], dc == 0 ? z : s[qb][kb]);
+            dp[qb][kb] = mfma16x16x32<F16>(qo[qb][dc][1], vreg[kb][dc], dc == 0 ? d4[qb] : dp[qb][kb]);
+          }
+    };
+    // P and dS of sub-block sb, packed as B operands: k index 8g + e stands for
+    // query 32*sb + 4g + e (e < 4, block qb = 0) or 32*sb + 16 + 4g + e - 4.
+    auto softmax_grad = [&](int sb, f32x4 (*s)[2], f32x4 (*dp)[2], const f32x4* l4, e16x8* pb,
+                            e16x8* gb) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          // query qt0 + 32sb + 16qb + 4g + i sees key keys[kb] iff i >= lo
+          const int lo = keys[kb] - (qt0 + sb * 32 + qb * 16 + 4 * g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float p = fast_exp2(fmaf(s[qb][kb][i], c2, -l4[qb][i]));
+            if (MASKED) p = i >= lo ? p : 0.f;
+            s[qb][kb][i] = p;
+            dp[qb][kb][i] = p * dp[qb][kb][i];
+          }
+        }
+        const u32x4 wp = {pack2<F16>(s[0][kb][0], s[0][kb][1]), pack2<F16>(s[0][kb][2], s[0][kb][3]),
+                          pack2<F16>(s[1][kb][0], s[1][kb][1]), pack2<F16>(s[1][kb][2], s[1][kb][3])};
+        const u32x4 wg = {pack2<F16>(dp[0][kb][0], dp[0][kb][1]), pack2<F16>(dp[0][kb][2], dp[0][kb][3]),
+                          pack2<F16>(dp[1][kb][0], dp[1][kb][1]), pack2<F16>(dp[1][kb][2], dp[1][kb][3])};
+        pb[kb] = as_e16x8(wp);
+        gb[kb] = as_e16x8(wg);
+      }
+    };
+    auto read_tr = [&](int sb, e16x8 (*qo)[2]) {  // qo[db] = {dO^T, Q^T}
+#pragma unroll
+      for (int db = 0; db < DBK; ++db) {
+        const int r0 = sb * 32 * (D * 2) + toff[db];
+        qo[db][0] = join_e16x8(lds_load_tr16(dOt + r0), lds_load_tr16(dOt + r0 + 16 * (D * 2)));
+        qo[db][1] = join_e16x8(lds_load_tr16(Qt + r0), lds_load_tr16(Qt + r0 + 16 * (D * 2)));
+      }
     };
     auto grad_mfma = [&](e16x8 (*qo)[2], const e16x8* pb, const e16x8* gb) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int db = 0; db < DBK; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dv[db] = mfma32x32x16<F16>(qo[h * DB + db][0], pb[h], dv[db]);
-          dk[db] = mfma32x32x16<F16>(qo[h * DB + db][1], gb[h], dk[db]);
+        for (int kb = 0; kb < 2; ++kb) {
+          dv[db][kb] = mfma16x16x32<F16>(qo[db][0], pb[kb], dv[db][kb]);
+          dk[db][kb] = mfma16x16x32<F16>(qo[db][1], gb[kb], dk[db][kb]);
         }
     };
 
@@ -289,69 +265,50 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     // laid out in phases separated by scheduling fences so that the exp/VALU
     // work of one sub-block runs under the MFMAs of the other and every LDS
     // read is issued a phase ahead of the MFMA that consumes it.
-    constexpr int PM = 2 * DS;  // MFMAs per phase
+    constexpr int PM = 8 * DC;  // MFMAs per phase
     // Phase 1a: statistics and Q/dO row operands of A.
-    e16x8 qa[DS], oa[DS];
-    f32x4 lA[4], dA[4];
-    read_stats(0, lA, dA);  // first: -delta_A is the dP_A accumulator's start
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      qa[ds] = ad.rowop(Qt, 0, ds);
-      oa[ds] = ad.rowop(dOt, 0, ds);
-    }
+    e16x8 ra[2][DC][2];
+    f32x4 lA[2], dA[2];
+    read_stats(0, lA, dA);
+    read_rows(0, ra);
     __builtin_amdgcn_sched_barrier(0);
-    // Phase 1b: S_A = Q_A K^T, dP_A = dO_A V^T - delta_A (the accumulator
-    // starts at the rows' -delta); reads: statistics and row operands of B.
-    f32x16 sA = mfma32x32x16_z<F16>(qa[0], kreg[0]);
-    f32x16 dpA = mfma32x32x16<F16>(oa[0], vreg[0], join16(dA));
-#pragma unroll
-    for (int ds = 1; ds < DS; ++ds) {
-      sA = mfma32x32x16<F16>(qa[ds], kreg[ds], sA);
-      dpA = mfma32x32x16<F16>(oa[ds], vreg[ds], dpA);
-    }
-    f32x4 lB[4], dB[4];
+    // Phase 1b: S_A, dP_A - delta_A; reads: statistics and row operands of B.
+    f32x4 sA[2][2], dpA[2][2];
+    scores(ra, dA, sA, dpA);
+    f32x4 lB[2], dB[2];
     read_stats(1, lB, dB);
-    e16x8 qb[DS], ob[DS];
+    e16x8 rb[2][DC][2];
+    read_rows(1, rb);
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      qb[ds] = ad.rowop(Qt, 32, ds);
-      ob[ds] = ad.rowop(dOt, 32, ds);
-    }
-#pragma unroll
-    for (int i = 0; i < PM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int i = 0; i < PM / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // Phase 2: S_B, dP_B - delta_B; VALU of A; reads: transposed operands of A.
-    f32x16 sB = mfma32x32x16_z<F16>(qb[0], kreg[0]);
-    f32x16 dpB = mfma32x32x16<F16>(ob[0], vreg[0], join16(dB));
-#pragma unroll
-    for (int ds = 1; ds < DS; ++ds) {
-      sB = mfma32x32x16<F16>(qb[ds], kreg[ds], sB);
-      dpB = mfma32x32x16<F16>(ob[ds], vreg[ds], dpB);
-    }
+    f32x4 sB[2][2], dpB[2][2];
+    scores(rb, dB, sB, dpB);
     e16x8 pA[2], gA[2];
     softmax_grad(0, sA, dpA, lA, pA, gA);
-    e16x8 trA[2 * DB][2];
+    e16x8 trA[DBK][2];
     read_tr(0, trA);
 #pragma unroll
-    for (int i = 0; i < PM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 6, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    for (int i = 0; i < PM / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // Phase 3: dV, dK += sub-block A; VALU of B; reads: transposed operands of B.
     grad_mfma(trA, pA, gA);
     e16x8 pB[2], gB[2];
     softmax_grad(1, sB, dpB, lB, pB, gB);
-    e16x8 trB[2 * DB][2];
+    e16x8 trB[DBK][2];
     read_tr(1, trB);
 #pragma unroll
-    for (int i = 0; i < PM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 6, 0);
+    for (int i = 0; i < PM / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, 5, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -365,8 +322,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   // heads run first and the unmasked tiles after, so each loop body holds one
   // variant of the tile code (with both in one loop the register allocator
   // went past its budget and spilled).
-  auto set_head = [&](int g) {
-    const size_t qoff = (size_t)(hq0 + g) * N;
+  auto set_head = [&](int hg) {
+    const size_t qoff = (size_t)(hq0 + hg) * N;
     qdma.head = (const e16_t*)a.q + qoff * D;
     odma.head = (const e16_t*)a.dO + qoff * D;
     lse2_h = a.lse2 + qoff;
@@ -375,8 +332,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   // Every loop iteration starts by filling stage 0, which is free: every wave
   // passed the barrier that ended the previous tile.
   if (CAUSAL) {  // query tiles [n0, n0 + 128): the diagonal
-    for (int g = 0; g < G; ++g) {
-      set_head(g);
+    for (int hg = 0; hg < G; ++hg) {
+      set_head(hg);
       load_tile(q_begin, 0);
       dma_wait();
       __syncthreads();
@@ -385,8 +342,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     }
   }
   const int t0 = CAUSAL ? 2 : 0;
-  for (int g = 0; g < G; ++g) {
-    set_head(g);
+  for (int hg = 0; hg < G; ++hg) {
+    set_head(hg);
     load_tile(q_begin + t0 * BM, 0);
     dma_wait();
     __syncthreads();
@@ -396,9 +353,22 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     }
   }
 
-  if (key < N) {
-    store_rowT<DB, F16>(dKh + (size_t)key * D, dk, a.scale, key < L, hi);
-    store_rowT<DB, F16>(dVh + (size_t)key * D, dv, 1.f, key < L, hi);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    if (keys[kb] < N) {
+      const bool kv = keys[kb] < L;
+      e16_t* krow = dKh + (size_t)keys[kb] * D;
+      e16_t* vrow = dVh + (size_t)keys[kb] * D;
+#pragma unroll
+      for (int db = 0; db < DBK; ++db) {
+        const u32x2 wk = {kv ? pack2<F16>(dk[db][kb][0] * a.scale, dk[db][kb][1] * a.scale) : 0u,
+                          kv ? pack2<F16>(dk[db][kb][2] * a.scale, dk[db][kb][3] * a.scale) : 0u};
+        const u32x2 wv = {kv ? pack2<F16>(dv[db][kb][0], dv[db][kb][1]) : 0u,
+                          kv ? pack2<F16>(dv[db][kb][2], dv[db][kb][3]) : 0u};
+        gstore8(krow + db * 16 + 4 * g, wk);
+        gstore8(vrow + db * 16 + 4 * g, wv);
+      }
+    }
   }
 }
 
