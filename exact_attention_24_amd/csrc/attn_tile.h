@@ -1,5 +1,7 @@
-// LDS tile layout and MFMA operand helpers shared by the forward and backward
-// kernels (gfx950, wave64, v_mfma_f32_32x32x16_bf16 / _f16).
+// LDS tile layouts, direct global->LDS tile loads and MFMA operand helpers
+// shared by the attention kernels (gfx950, wave64). The forward and backward
+// read 16x16x32 MFMA operands from the TILE_K16 / TILE_T16 layouts below; the
+// decode reads 32x32x16 operands from the swz layout.
 #pragma once
 
 #include "attn_common.h"
@@ -7,10 +9,10 @@
 namespace attn {
 
 // A row-major [rows][D] 16-bit tile in LDS, no padding; the 16-byte chunk c of
-// row r sits at chunk c ^ swz(r). The XOR keeps both read patterns free of
-// bank conflicts on gfx950's 64 LDS banks: 16 consecutive rows read at one
-// chunk (ds_read_b128 operands), and 4 consecutive rows read as 4 consecutive
-// chunks (ds_read_b64_tr_b16 transposed operands). It is a bijection on the
+// row r sits at chunk c ^ swz(r). The XOR keeps the 32x32x16 operand reads
+// free of bank conflicts on gfx950's 64 LDS banks: 32 consecutive rows read at
+// two chunks (ds_read_b128 operands), and 4 consecutive rows read as 4
+// consecutive chunks (ds_read_b64_tr_b16 transposed operands). It is a bijection on the
 // chunks of each row, so a wave can fill whole rows with one 1 KB
 // global_load_lds_dwordx4 by fetching, for physical chunk p, logical chunk
 // p ^ swz(r).
@@ -26,13 +28,16 @@ __device__ __forceinline__ int tile_off(int r, int chunk) {
   return r * (D * 2) + ((chunk ^ swz<D>(r)) << 4);
 }
 
-// Two more layouts for 128-column tiles read only by 16x16x32 MFMA operands
-// (both bijections on each row's chunks; measured free of bank conflicts with
-// SQ_LDS_BANK_CONFLICT, where swz above is not for the first pattern):
+// Two more layouts for tiles read by 16x16x32 MFMA operands (both bijections
+// on each row's chunks; measured with SQ_LDS_BANK_CONFLICT, against which swz
+// above conflicts for the first pattern):
 //  - TILE_K16, for ds_read_b128 operands that take 16 consecutive rows at 4
-//    consecutive chunks: chunk c of row r at c ^ (r % 16);
+//    consecutive chunks: chunk c of row r at c ^ (r % 16) for 128 columns,
+//    c ^ ((r / 2) % 8) for 64 (two rows per bank line); conflict-free;
 //  - TILE_T16, for transposing reads that take eight consecutive rows at two
-//    consecutive chunks per half-wave: chunk c of row r at c ^ (2 * (r % 8)).
+//    consecutive chunks per half-wave: chunk c of row r at c ^ (2 * (r % 8)),
+//    or c ^ (2 * ((r / 2) % 4)) for 64 columns; conflict-free for those reads
+//    and, as measured in the backward kernels, for the b128 pattern above too.
 enum TileLayout { TILE_SWZ = 0, TILE_K16 = 1, TILE_T16 = 2 };
 template <int D, int LAYOUT>
 __device__ __forceinline__ int layout_swz(int r) {
