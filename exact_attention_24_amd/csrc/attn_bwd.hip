@@ -177,33 +177,41 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) { dk[db][kb][i] = 0.f; dv[db][kb][i] = 0.f; }
 
+  // Statistics and Q/dO row operands of sub-block sb of the tile in stage st:
+  // queries 32*sb + 16*qb + 4*g + i in the accumulators.
+  auto read_stats = [&](int st, int sb, f32x4* l4, f32x4* d4) {
+    const lds_t* lse_t = lds_base(st ? st1_ : st0_);
+    const lds_t* del_t = lse_t + BM * 4;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int rl = sb * 32 + qb * 16 + g * 4;
+      l4[qb] = *(const ATTN_LDS f32x4*)(lse_t + rl * 4);
+      d4[qb] = *(const ATTN_LDS f32x4*)(del_t + rl * 4);
+    }
+  };
+  auto read_rows = [&](int st, int sb, e16x8 (*qo)[DC][2]) {  // qo[qb][dc] = {Q, dO}
+    const lds_t* Qt = lds_base(st ? q1_ : q0_);
+    const lds_t* dOt = lds_base(st ? o1_ : o0_);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const int r0 = (sb * 32 + qb * 16) * (D * 2);
+        qo[qb][dc][0] = as_e16x8(lds_load16(Qt + r0 + roff[dc]));
+        qo[qb][dc][1] = as_e16x8(lds_load16(dOt + r0 + roff[dc]));
+      }
+  };
+  // Sub-block A's operands are read one phase early: the step before issues
+  // them under its last MFMAs (the loop prologues issue the first ones).
+  e16x8 ra[2][DC][2];
+  f32x4 lA[2], dA[2];
+
   auto step = [&](int t, const int st, const bool MASKED) {
     const int qt0 = q_begin + t * BM;
     load_tile(qt0 + BM, st ^ 1);
     const lds_t* Qt = lds_base(st ? q1_ : q0_);
     const lds_t* dOt = lds_base(st ? o1_ : o0_);
-    const lds_t* lse_t = lds_base(st ? st1_ : st0_);
-    const lds_t* del_t = lse_t + BM * 4;
 
-    // Sub-block sb: queries qt0 + 32*sb + 16*qb + 4*g + i in the accumulators.
-    auto read_stats = [&](int sb, f32x4* l4, f32x4* d4) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int rl = sb * 32 + qb * 16 + g * 4;
-        l4[qb] = *(const ATTN_LDS f32x4*)(lse_t + rl * 4);
-        d4[qb] = *(const ATTN_LDS f32x4*)(del_t + rl * 4);
-      }
-    };
-    auto read_rows = [&](int sb, e16x8 (*qo)[DC][2]) {  // qo[qb][dc] = {Q, dO}
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const int r0 = (sb * 32 + qb * 16) * (D * 2);
-          qo[qb][dc][0] = as_e16x8(lds_load16(Qt + r0 + roff[dc]));
-          qo[qb][dc][1] = as_e16x8(lds_load16(dOt + r0 + roff[dc]));
-        }
-    };
     // S = Q K^T and dP - delta = dO V^T - delta (the accumulator starts at -delta).
     auto scores = [&](e16x8 (*qo)[DC][2], const f32x4* d4, f32x4 (*s)[2], f32x4 (*dp)[2]) {
 #pragma unroll
@@ -266,19 +274,13 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     // work of one sub-block runs under the MFMAs of the other and every LDS
     // read is issued a phase ahead of the MFMA that consumes it.
     constexpr int PM = 8 * DC;  // MFMAs per phase
-    // Phase 1a: statistics and Q/dO row operands of A.
-    e16x8 ra[2][DC][2];
-    f32x4 lA[2], dA[2];
-    read_stats(0, lA, dA);
-    read_rows(0, ra);
-    __builtin_amdgcn_sched_barrier(0);
-    // Phase 1b: S_A, dP_A - delta_A; reads: statistics and row operands of B.
+    // Phase 1: S_A, dP_A - delta_A; reads: statistics and row operands of B.
     f32x4 sA[2][2], dpA[2][2];
     scores(ra, dA, sA, dpA);
     f32x4 lB[2], dB[2];
-    read_stats(1, lB, dB);
+    read_stats(st, 1, lB, dB);
     e16x8 rb[2][DC][2];
-    read_rows(1, rb);
+    read_rows(st, 1, rb);
 #pragma unroll
     for (int i = 0; i < PM / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -312,10 +314,21 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Phase 4: dV, dK += sub-block B.
-    grad_mfma(trB, pB, gB);
+    // The next tile has landed (this wave's loads, then every wave's) and no
+    // wave reads this stage any more; phase 4 reads nothing from LDS.
     dma_wait();
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase 4: dV, dK += sub-block B; reads: sub-block A of the next tile.
+    grad_mfma(trB, pB, gB);
+    read_stats(st ^ 1, 0, lA, dA);
+    read_rows(st ^ 1, 0, ra);
+#pragma unroll
+    for (int i = 0; i < PM / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (i < 10) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Heads of the group one after another; the causal diagonal pairs of all
@@ -329,14 +342,18 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     lse2_h = a.lse2 + qoff;
     delta_h = a.delta + qoff;
   };
-  // Every loop iteration starts by filling stage 0, which is free: every wave
-  // passed the barrier that ended the previous tile.
+  // Every loop iteration starts by filling stage 0 once every wave is past
+  // its last read of it (the early reads of the step before, whose values
+  // are not used), then reads sub-block A of that tile.
   if (CAUSAL) {  // query tiles [n0, n0 + 128): the diagonal
     for (int hg = 0; hg < G; ++hg) {
       set_head(hg);
+      __syncthreads();
       load_tile(q_begin, 0);
       dma_wait();
       __syncthreads();
+      read_stats(0, 0, lA, dA);
+      read_rows(0, 0, ra);
       step(0, 0, true);
       step(1, 1, true);
     }
@@ -344,9 +361,12 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   const int t0 = CAUSAL ? 2 : 0;
   for (int hg = 0; hg < G; ++hg) {
     set_head(hg);
+    __syncthreads();
     load_tile(q_begin + t0 * BM, 0);
     dma_wait();
     __syncthreads();
+    read_stats(0, 0, lA, dA);
+    read_rows(0, 0, ra);
     for (int t = t0; t < nqt; t += 2) {
       step(t, 0, false);
       step(t + 1, 1, false);
