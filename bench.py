@@ -6,29 +6,44 @@ Q/K/V resident in device memory before the timed region. FLOPs are counted as
 4*B*H*N^2*d, halved for the causal mask (only the lower triangle is work).
 Prints ONE JSON line.
 
-Timing follows the method of the AIInfra FlashAttention note (dpshk.com,
-§3.2): warm-up launches first, device synchronisation on both sides of the
-timed region, a HIP event pair around each kernel launch on the stream the
-kernel runs on, median reported alongside the mean. `value` is the wall-clock
-throughput of the timed region. A second pass runs the same number of launches
-back to back with one event pair around all of them; its per-launch time is
-reported too (on this power-limited GPU, back-to-back launches can run a few
-percent slower or faster than launches separated by the event records).
+Timed region: `--warmup` untimed launches, a device synchronisation, then
+`--steps` launches back to back with one HIP event pair on the launch stream
+around all of them, and a synchronisation. `value` is the region's wall-clock
+rate; `roofline.achieved` divides the FLOPs of one launch by the kernel's
+average launch duration (the event pair's time / steps).
+
+Distribution pass (the method of the AIInfra FlashAttention note, dpshk.com,
+§3.2: median and P90 of launches timed one by one): the same launches again,
+each with its own event pair, each preceded (outside its event pair) by a
+read of a 512 MiB buffer, larger than the 256 MiB Infinity Cache, so every
+timed launch starts with its inputs in HBM only and no dirty lines in the
+caches ("cold").
+
+Before the warm-up launches of each measurement the kernel runs back to back,
+untimed, for `--settle-ms` of wall time: on this power-managed GPU the clock
+under load takes that long to settle, and a few warm-up launches alone would
+time the ramp instead of the kernel.
+
+The same line carries, under extra keys, every other workload measured the
+same two ways: the fp32, d=64 and padded-batch forwards, the forward of the
+N=8192 workload, fp16 and grouped-query forwards, the context sweep
+N = 2K/4K/8K/16K, the backward (bf16, fp16, grouped) and the three decode
+workloads against the HBM roofline (cold and warm).
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
-import statistics
 import sys
 import time
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 WORKLOAD = "causal_bf16_b2_h32_n4096_d128"
 METRIC = "attention fwd TFLOPS (and % of bf16 MFMA peak) at B=2,H=32,N=4096,d=128 causal"
+FLUSH_BYTES = 512 << 20     # larger than the 256 MiB Infinity Cache
 
 
 def fwd_flops(B, H, N, d, causal):
@@ -131,157 +146,144 @@ def copy_calibration(torch, steps):
                       "bytes_written_per_launch": COPY_BYTES, "launches": steps}), flush=True)
 
 
-def gemm_reference(torch, steps, warmup):
-    """A plain bf16 library GEMM (torch.matmul, 8192 x 8192 x 8192) timed the same
-    way as the forward, once on seeded random operands and once on zeros: the
-    dense-MFMA rate a vendor kernel reaches on this GPU under the same power
-    limit, as context for the attention kernel's fraction of the nominal peak."""
-    n = 8192
-    g = torch.Generator("cpu").manual_seed(1234)
-    a = torch.randn(n, n, generator=g).to(torch.bfloat16).to("cuda:0")
-    b = torch.randn(n, n, generator=g).to(torch.bfloat16).to("cuda:0")
-    c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda:0")
-    for kind in ("random", "zeros"):
-        if kind == "zeros":
-            a.zero_()
-            b.zero_()
+class Timer:
+    """The two timing passes shared by every measurement (see the module
+    docstring). Both use HIP events recorded on the stream the kernels are
+    launched on."""
+
+    def __init__(self, torch, dev, settle_ms=0.0):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream(dev)
+        self.settle_ms = settle_ms
+        self.flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        self.evict()
+        self.evict()
+
+    def evict(self):
+        """Read the 512 MiB buffer: every cache line of the L2s and the Infinity
+        Cache is then one of its lines, and clean (a read, unlike a write, leaves
+        no dirty lines for the next kernel to write back)."""
+        return self.flush.sum()
+
+    def settle(self, fn):
+        """Launch fn back to back for settle_ms of wall time (untimed): the
+        power-managed clock takes a while under load to reach its steady state."""
+        if self.settle_ms <= 0:
+            return
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < self.settle_ms:
+            for _ in range(8):
+                fn()
+            self.torch.cuda.synchronize()
+
+    def region(self, fn, steps, warmup):
+        """Back-to-back launches: (wall ms per step, event ms per launch)."""
+        torch = self.torch
+        self.settle(fn)
         for _ in range(warmup):
-            torch.matmul(a, b, out=c)
+            fn()
         torch.cuda.synchronize()
-        times = []
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(self.stream)
         for _ in range(steps):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            torch.matmul(a, b, out=c)
-            e1.record()
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1))
-        med = statistics.median(times)
-        print(json.dumps({"mode": "gemm", "op": "torch.matmul bf16", "M": n, "N": n, "K": n,
-                          "values": kind, "ms_median": round(med, 4),
-                          "tflops": round(2.0 * n ** 3 / med / 1e9, 1)}), flush=True)
+            fn()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+    def cold(self, fn, n):
+        """n launches timed one by one, each after a 512 MiB read (outside its
+        event pair); sorted ms."""
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, b in ev:
+            self.evict()
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)
 
 
-BWD_WORKLOAD = "causal_fwdbwd_bf16_b2_h16_n8192_d128"
+def stats(per):
+    med, p90 = per[len(per) // 2], per[int(0.9 * (len(per) - 1))]
+    return med, p90
 
 
-def bench_backward(torch, ea, steps, warmup=3):
-    """Time the recompute backward (delta, dK/dV and dQ kernels) on the causal
-    B=2 H=16 N=8192 d=128 workload, with O and LSE from one forward pass.
-    FLOPs follow the 5-GEMM convention, 10*B*H*N^2*d halved for causal; the
-    kernels execute 7 GEMMs' worth (S and dP are recomputed for dQ)."""
-    from attn_inputs import WORKLOADS, make_workload_inputs
-    w = WORKLOADS[BWD_WORKLOAD]
+def rate(work, ms, scale=1e12):
+    return work / (ms * 1e-3) / scale
+
+
+def fwd_case(torch, ea, timer, w, steps, warmup, x=None, dev="cuda:0"):
+    """One forward workload: timed region and cold distribution. Inputs are the
+    workload's seeded draws (or, for sweep cases without ``seed`` inputs,
+    seeded normal draws on the device)."""
+    from attn_inputs import make_workload_inputs
+    if x is None:
+        x = make_workload_inputs(w)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    seqlens = x["seqlens"].to(dev) if x.get("seqlens") is not None else None
+    lens = x["seqlens"].tolist() if seqlens is not None else [w.N] * w.B
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    flops = sum(fwd_flops(1, w.H, L, w.d, w.causal) for L in lens)
+    fn = lambda: ea.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, seqlens=seqlens, out=o, lse=lse)
+    wall_ms, ev_ms = timer.region(fn, steps, warmup)
+    med, p90 = stats(timer.cold(fn, steps))
+    peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    return {"B": w.B, "H": w.H, "H_kv": w.kv_heads, "N": w.N, "d": w.d, "dtype": w.dtype,
+            "causal": w.causal, "varlen": seqlens is not None, "gflop": round(flops / 1e9, 3),
+            "ms_back_to_back": round(ev_ms, 4), "ms_wall_per_step": round(wall_ms, 4),
+            "ms_median_cold": round(med, 4), "ms_p90_cold": round(p90, 4),
+            "tflops_back_to_back": round(rate(flops, ev_ms), 1),
+            "tflops_median_cold": round(rate(flops, med), 1),
+            "frac_of_peak": round(rate(flops, ev_ms) / peak, 4),
+            "peak_tflops": peak, "flop_convention": "4*H*sum_b L_b^2*d, halved if causal"}
+
+
+def bwd_case(torch, ea, timer, w, steps, warmup, dev="cuda:0"):
+    """The recompute backward (delta, dK/dV and dQ kernels) on a workload with
+    dO, with O and LSE from one forward pass. FLOPs follow the 5-GEMM
+    convention, 10*B*H*N^2*d halved for causal; the kernels execute 7 GEMMs'
+    worth (S and dP are recomputed for dQ)."""
+    from attn_inputs import make_workload_inputs
     x = make_workload_inputs(w)
-    dev = torch.device("cuda:0")
     q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
     o, lse = ea.attn_fwd(q, k, v, scale=w.scale, causal=w.causal)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(ea.attn_bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step():
-        ea.attn_bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
-                    workspace=ws)
-
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    per = sorted(a.elapsed_time(b) for a, b in ev)
-    mean_ms = sum(per) / len(per)
-    flops = 10.0 * w.B * w.H * w.N * w.N * w.d / 2
-    executed = 14.0 * w.B * w.H * w.N * w.N * w.d / 2
-    return {"workload": BWD_WORKLOAD, "ms_mean": round(mean_ms, 4), "ms_median": round(per[len(per) // 2], 4),
-            "tflops": round(flops / (mean_ms * 1e-3) / 1e12, 2),
-            "tflops_executed": round(executed / (mean_ms * 1e-3) / 1e12, 2),
-            "frac_of_bf16_peak": round(flops / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "flop_convention": "10*B*H*N^2*d/2 (5 GEMMs, causal half); executed = 14*B*H*N^2*d/2"}
-
-
-SUITE_WORKLOADS = ["mha_bf16_b4_h16_n2048_d64", "causal_bf16_b2_h32_n4096_d128",
-                   "varlen_bf16_b8_h16_n2048_d128", "causal_fwdbwd_bf16_b2_h16_n8192_d128",
-                   "gqa_causal_bf16_b2_h32_hkv8_n4096_d128", "causal_f16_b2_h32_n4096_d128"]
-SWEEP_N = [2048, 4096, 8192, 16384]
-FLUSH_BYTES = 512 << 20  # larger than the 256 MiB Infinity Cache
-
-
-def time_launches(torch, fn, stream, warmup, steps):
-    """Per-launch HIP-event times (ms), sorted, after `warmup` untimed launches."""
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for a, b in ev:
-        a.record(stream)
-        fn()
-        b.record(stream)
-    torch.cuda.synchronize()
-    return sorted(a.elapsed_time(b) for a, b in ev)
-
-
-def bench_suite(torch, ea, steps, warmup):
-    """Forward timings of every workload and of a context sweep (B=2 H=32 d=128
-    causal, N = 2K..16K). A 512 MiB buffer is written before each case so no
-    case starts with its inputs in the Infinity Cache. One JSON line per case:
-    median and P90 launch times and TFLOPS at the median."""
-    from attn_inputs import WORKLOADS, make_workload_inputs, Workload
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-    cases = [(WORKLOADS[n], None) for n in SUITE_WORKLOADS]
-    cases += [(Workload(f"sweep_causal_bf16_b2_h32_n{n}_d128", 2, 32, n, 128, "bf16", True, 2000 + n), n)
-              for n in SWEEP_N]
-    for w, sweep_n in cases:
-        if sweep_n is None:
-            x = make_workload_inputs(w)
-            q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
-            seqlens = x["seqlens"].to(dev) if x.get("seqlens") is not None else None
-            lens = x["seqlens"].tolist() if seqlens is not None else [w.N] * w.B
-        else:  # timing only: seeded normal inputs drawn on the device
-            g = torch.Generator(device=dev)
-            g.manual_seed(w.seed)
-            q, k, v = (torch.randn((w.B, w.H, w.N, w.d), generator=g, device=dev).to(torch.bfloat16)
-                       for _ in range(3))
-            seqlens, lens = None, [w.N] * w.B
-        o = torch.empty_like(q)
-        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-        flops = sum(fwd_flops(1, w.H, L, w.d, w.causal) for L in lens)
-        flush.fill_(1)
-        per = time_launches(torch, lambda: ea.attn_fwd(q, k, v, scale=w.scale, causal=w.causal,
-                                                       seqlens=seqlens, out=o, lse=lse),
-                            stream, warmup, steps)
-        med, p90 = per[len(per) // 2], per[int(0.9 * (len(per) - 1))]
-        print(json.dumps({"mode": "suite", "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                          "causal": w.causal, "varlen": seqlens is not None,
-                          "gflop": round(flops / 1e9, 2), "ms_median": round(med, 4),
-                          "ms_p90": round(p90, 4), "tflops_median": round(flops / (med * 1e-3) / 1e12, 1),
-                          "pct_of_bf16_peak": round(100 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)}),
-              flush=True)
-        del q, k, v, o, lse
+    fn = lambda: ea.attn_bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal, dq=dq, dk=dk,
+                             dv=dv, workspace=ws)
+    wall_ms, ev_ms = timer.region(fn, steps, warmup)
+    med, p90 = stats(timer.cold(fn, steps))
+    flops = 10.0 * w.B * w.H * w.N * w.N * w.d / (2 if w.causal else 1)
+    return {"B": w.B, "H": w.H, "H_kv": w.kv_heads, "N": w.N, "d": w.d, "dtype": w.dtype,
+            "causal": w.causal, "ms_back_to_back": round(ev_ms, 4),
+            "ms_median_cold": round(med, 4), "ms_p90_cold": round(p90, 4),
+            "tflops": round(rate(flops, ev_ms), 2),
+            "tflops_executed": round(rate(flops * 1.4, ev_ms), 2),
+            "frac_of_bf16_peak": round(rate(flops, ev_ms) / PEAK_BF16_TFLOPS, 4),
+            "flop_convention": "10*B*H*N^2*d/2 (5 GEMMs, causal half); executed = 7 GEMMs"}
 
 
 DECODE_WORKLOADS = ["decode_bf16_b8_h64_hkv8_nq1_nk8192_d128", "decode_bf16_b8_h64_hkv8_nq8_nk8192_d128",
                     "decode_fp8kv_bf16_b8_h64_hkv8_nq1_nk8192_d128"]
 
 
-def bench_decode(torch, ea, name, steps, warmup):
-    """Time one split-KV decode call (split kernel + merge) on a decode
-    workload. Decode is bound by HBM bandwidth ("Attention 算子优化..." §五), so the roofline
-    is bytes: K and V over every valid cached position once, Q read, O and LSE
-    written, divided by the median call time, against 8 TB/s."""
+def decode_case(torch, ea, timer, name, steps, warmup, dev="cuda:0"):
+    """One split-KV decode call (split kernel + merge). Decode is bound by HBM
+    bandwidth ("Attention 算子优化..." §五), so the roofline is bytes: K and V
+    over every valid cached position once, Q read, O and LSE written, against
+    8 TB/s. Cold: each call after a 512 MiB read, so the cache comes from
+    HBM (the FP8 cache, ~139 MB, and the bf16 one, ~268 MB, would otherwise
+    sit in the 256 MiB Infinity Cache); warm: calls back to back."""
     from attn_inputs import WORKLOADS, fp8_cache, make_workload_inputs
     w = WORKLOADS[name]
     x = make_workload_inputs(w)
-    dev = torch.device("cuda:0")
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
     if w.kv_fp8:  # FP8 (E4M3) cache with per-token scales, built once before timing
         k8, ks = (t.to(dev) for t in fp8_cache(x["k"]))
@@ -292,26 +294,96 @@ def bench_decode(torch, ea, name, steps, warmup):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     ws = torch.empty(ea.attn_decode_workspace_bytes(w.B, w.H, w.kv_heads, w.Nq, w.N, w.d),
                      dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-    flush.fill_(1)
     if w.kv_fp8:
         fn = lambda: ea.attn_decode_fp8kv(q, k8, v8, ks, vs, scale=w.scale, causal=w.causal,
                                           kv_lens=kl, out=o, lse=lse, workspace=ws)
     else:
         fn = lambda: ea.attn_decode(q, k, v, scale=w.scale, causal=w.causal, kv_lens=kl, out=o,
                                     lse=lse, workspace=ws)
-    per = time_launches(torch, fn, stream, warmup, steps)
-    med = per[len(per) // 2]
+    _, warm_ms = timer.region(fn, steps, warmup)
+    med, p90 = stats(timer.cold(fn, steps))
     # K and V: 2 bytes per element, or 1 byte plus a 4-byte scale per token
     kv_bytes = sum(lens) * w.kv_heads * 2 * ((w.d + 4) if w.kv_fp8 else w.d * 2)
     io_bytes = w.B * w.H * w.Nq * (w.d * 2 * 2 + 4)
-    gbs = (kv_bytes + io_bytes) / (med * 1e-3) / 1e9
-    return {"workload": name, "ms_median": round(med, 4), "ms_p90": round(per[int(0.9 * (len(per) - 1))], 4),
-            "algorithmic_bytes": kv_bytes + io_bytes, "achieved_GBps": round(gbs, 1),
-            "peak_GBps": PEAK_HBM_GBS, "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+    nbytes = kv_bytes + io_bytes
+    return {"ms_median_cold": round(med, 4), "ms_p90_cold": round(p90, 4),
+            "ms_back_to_back_warm": round(warm_ms, 4), "algorithmic_bytes": nbytes,
+            "GBps_median_cold": round(rate(nbytes, med, 1e9), 1),
+            "GBps_back_to_back_warm": round(rate(nbytes, warm_ms, 1e9), 1),
+            "frac_of_hbm_peak": round(rate(nbytes, med, 1e9) / PEAK_HBM_GBS, 4),
+            "peak_GBps": PEAK_HBM_GBS,
             "kv_format": "fp8 e4m3 + per-token fp32 scale" if w.kv_fp8 else w.dtype,
-            "bytes_convention": "K,V over every valid cached position + Q read + O, LSE written"}
+            "bytes_convention": "K,V over every valid cached position + Q read + O, LSE written; "
+                                "frac from the cold median"}
+
+
+SUITE_WORKLOADS = ["single_head_f32_n256_d64", "mha_bf16_b4_h16_n2048_d64", "varlen_bf16_b8_h16_n2048_d128",
+                   "causal_fwdbwd_bf16_b2_h16_n8192_d128", "causal_f16_b2_h32_n4096_d128",
+                   "gqa_causal_bf16_b2_h32_hkv8_n4096_d128"]
+BWD_WORKLOADS = ["causal_fwdbwd_bf16_b2_h16_n8192_d128", "causal_f16_b2_h32_n4096_d128",
+                 "gqa_causal_bf16_b2_h32_hkv8_n4096_d128"]
+SWEEP_N = [2048, 4096, 8192, 16384]
+
+
+def sweep_inputs(torch, w, dev):
+    """Seeded normal inputs drawn on the device (timing only)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    q, k, v = (torch.randn((w.B, w.H, w.N, w.d), generator=g, device=dev).to(torch.bfloat16)
+               for _ in range(3))
+    return {"q": q, "k": k, "v": v, "seqlens": None}
+
+
+def extras(torch, ea, timer, steps, warmup, log, parts=("suite", "sweep", "bwd", "decode")):
+    """Every other forward workload, the context sweep, the backward and the
+    decode workloads (one dict each); ``parts`` selects which."""
+    from attn_inputs import WORKLOADS, Workload
+    out = {}
+    if "suite" in parts:
+        out["suite"] = {}
+        for name in SUITE_WORKLOADS:
+            log(f"suite {name}")
+            out["suite"][name] = fwd_case(torch, ea, timer, WORKLOADS[name], steps, warmup)
+    if "sweep" in parts:
+        out["sweep"] = {}
+        for n in SWEEP_N:
+            w = Workload(f"sweep_causal_bf16_b2_h32_n{n}_d128", 2, 32, n, 128, "bf16", True, 2000 + n)
+            log(f"sweep N={n}")
+            out["sweep"][w.name] = fwd_case(torch, ea, timer, w, steps, warmup,
+                                            x=sweep_inputs(torch, w, "cuda:0"))
+    if "bwd" in parts:
+        out["bwd_suite"] = {}
+        for name in BWD_WORKLOADS:
+            log(f"backward {name}")
+            out["bwd_suite"][name] = bwd_case(torch, ea, timer, WORKLOADS[name], max(steps // 2, 5),
+                                              max(warmup // 2, 2))
+    if "decode" in parts:
+        out["decode"] = {}
+        for name in DECODE_WORKLOADS:
+            log(f"decode {name}")
+            out["decode"][name] = decode_case(torch, ea, timer, name, steps, warmup)
+    return out
+
+
+def gemm_reference(torch, steps, warmup):
+    """A plain bf16 library GEMM (torch.matmul, 8192 x 8192 x 8192) timed the same
+    way as the forward, once on seeded random operands and once on zeros: the
+    dense-MFMA rate a vendor kernel reaches on this GPU under the same power
+    limit, as context for the attention kernel's fraction of the nominal peak."""
+    n = 8192
+    g = torch.Generator("cpu").manual_seed(1234)
+    a = torch.randn(n, n, generator=g).to(torch.bfloat16).to("cuda:0")
+    b = torch.randn(n, n, generator=g).to(torch.bfloat16).to("cuda:0")
+    c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda:0")
+    timer = Timer(torch, torch.device("cuda:0"), 200.0)
+    for kind in ("random", "zeros"):
+        if kind == "zeros":
+            a.zero_()
+            b.zero_()
+        _, ms = timer.region(lambda: torch.matmul(a, b, out=c), steps, warmup)
+        print(json.dumps({"mode": "gemm", "op": "torch.matmul bf16", "M": n, "N": n, "K": n,
+                          "values": kind, "ms_back_to_back": round(ms, 4),
+                          "tflops": round(2.0 * n ** 3 / ms / 1e9, 1)}), flush=True)
 
 
 def main():
@@ -321,21 +393,23 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 disables it)")
-    ap.add_argument("--bwd-steps", type=int, default=10,
-                    help="timed backward passes on the causal B=2 H=16 N=8192 d=128 workload "
-                         "(reported under \"bwd\"; 0 skips them)")
-    ap.add_argument("--mode", choices=["fwd", "bwd", "copy", "suite", "decode", "gemm"], default="fwd",
-                    help="fwd: the benchmark; bwd: the backward alone; suite: forward timings "
-                         "of every workload plus a context sweep (one JSON line each); decode: "
-                         "the split-KV decode workloads against the HBM roofline; copy: a "
-                         "plain device copy of known size, whose FETCH_SIZE/WRITE_SIZE counters "
-                         "calibrate the traffic figure; gemm: a library bf16 GEMM on random "
-                         "and on zero operands, the dense-MFMA rate reachable under this "
-                         "GPU's power limit (context only)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed back-to-back launches before each measurement's warm-up, "
+                         "in ms of wall time (0: none)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline workload (no other workloads, sweep, backward or decode)")
+    ap.add_argument("--mode", choices=["fwd", "suite", "sweep", "bwd", "decode", "copy", "gemm"],
+                    default="fwd",
+                    help="fwd: the benchmark line; suite / sweep / bwd / decode: only that part "
+                         "of the line's extra measurements (one JSON line), for profiling one "
+                         "kernel family; copy: a plain device copy of known size, whose "
+                         "FETCH_SIZE/WRITE_SIZE counters calibrate the traffic figure; gemm: a "
+                         "library bf16 GEMM on random and on zero operands, the dense-MFMA rate "
+                         "reachable under this GPU's power limit (context only)")
     ap.add_argument("--values", choices=["random", "zeros"], default="random",
-                    help="fwd mode only: 'zeros' runs the same launches on all-zero Q, K, V, "
-                         "a diagnostic of data-dependent power (the clock the chip holds under "
-                         "MFMA load depends on operand bit activity); never the benchmark line")
+                    help="'zeros' runs the headline launches on all-zero Q, K, V, a diagnostic of "
+                         "data-dependent power (the clock the chip holds under MFMA load depends "
+                         "on operand bit activity); never the benchmark line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -350,62 +424,29 @@ def main():
         gemm_reference(torch, args.steps, args.warmup)
         return
     import exact_attention_24_amd as ea
-    if args.mode == "bwd":
-        print(json.dumps({"mode": "bwd", **bench_backward(torch, ea, args.steps, args.warmup)}), flush=True)
-        return
-    if args.mode == "suite":
-        bench_suite(torch, ea, args.steps, args.warmup)
-        return
-    if args.mode == "decode":
-        for name in DECODE_WORKLOADS:
-            print(json.dumps({"mode": "decode", **bench_decode(torch, ea, name, args.steps, args.warmup)}),
-                  flush=True)
-        return
     from attn_inputs import WORKLOADS, make_workload_inputs
 
-    w = WORKLOADS[WORKLOAD]
-    x = make_workload_inputs(w)
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    if args.mode in ("suite", "sweep", "bwd", "decode"):
+        part = extras(torch, ea, Timer(torch, dev, args.settle_ms), args.steps, args.warmup, log,
+                      parts=(args.mode,))
+        print(json.dumps({"mode": args.mode, **part}), flush=True)
+        return
+    w = WORKLOADS[WORKLOAD]
+    x = make_workload_inputs(w)
+    xd = dict(x)
     if args.values == "zeros":
-        q, k, v = (torch.zeros_like(t) for t in (q, k, v))
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step():
-        ea.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))  # ms per launch
-    mean_ms = sum(per) / len(per)
-    median_ms = per[len(per) // 2]
-    ms_per_step = wall * 1e3 / args.steps
-    # Second pass: the same launches back to back, one event pair around all.
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    b2b_ms = e0.elapsed_time(e1) / args.steps
+        xd = {n: (torch.zeros_like(t) if n in ("q", "k", "v") else t) for n, t in x.items()}
+    timer = Timer(torch, dev, args.settle_ms)
+    log(f"headline {WORKLOAD}")
+    head = fwd_case(torch, ea, timer, w, args.steps, args.warmup, x=xd)
     flops = fwd_flops(w.B, w.H, w.N, w.d, w.causal)
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (mean_ms * 1e-3) / 1e12
+    value = rate(flops, head["ms_wall_per_step"])
+    achieved = rate(flops, head["ms_back_to_back"])
 
     out = {
         "metric": METRIC,
@@ -414,7 +455,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_wall_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -423,25 +464,29 @@ def main():
         "config": {"workload": WORKLOAD, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "settle_ms": args.settle_ms,
         "device": device_info(torch),
-        "kernel_ms": {"mean": round(mean_ms, 4), "median": round(median_ms, 4),
-                      "p90": round(per[int(0.9 * (len(per) - 1))], 4),
-                      "back_to_back_per_launch": round(b2b_ms, 4)},
+        "kernel_ms": {"mean_back_to_back": head["ms_back_to_back"],
+                      "median_cold": head["ms_median_cold"], "p90_cold": head["ms_p90_cold"],
+                      "tflops_median_cold": head["tflops_median_cold"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic(),
                      "kernel": "fwd_16_kernel<128, causal, bf16>",
-                     "algorithmic": "4*B*H*N^2*d/2 FLOP per launch"},
+                     "algorithmic": "4*B*H*N^2*d/2 FLOP per launch; duration = HIP event pair "
+                                    "over the timed region / steps"},
     }
     if args.values == "zeros":
         out["data"] = "synthetic, all-zero Q/K/V (power diagnostic, not the benchmark)"
         out["roofline"]["traffic"] = None
         print(json.dumps(out), flush=True)
         return
-    if args.bwd_steps > 0:
-        out["bwd"] = bench_backward(torch, ea, args.bwd_steps)
-        out["decode"] = bench_decode(torch, ea, DECODE_WORKLOADS[0], 20, 5)
+    if not args.no_extras:
+        ext = extras(torch, ea, timer, args.steps, args.warmup, log)
+        out["bwd"] = ext["bwd_suite"]["causal_fwdbwd_bf16_b2_h16_n8192_d128"]
+        out.update(ext)
     if args.cpu_budget > 0:
+        log("cpu baseline")
         out["cpu_baseline"] = cpu_baseline(x, w, args.cpu_budget)
     print(json.dumps(out), flush=True)
 

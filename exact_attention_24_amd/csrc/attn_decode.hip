@@ -238,20 +238,40 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
     // are weighted against the reference without taking their max; a weight
     // above 2^8 forces the lane's partial sum above 2^8, and only then (rare)
     // does the reference move to the exact max, rescaling O and l.
-    if (t == 0) m_ref = fmaxf(m_ref, chunk_max(sc));
-    const f32x16 raw = sc;
-    float sum = weights(sc);
-    if (__builtin_amdgcn_ballot_w64(!(sum <= kLazyRescaleDecW))) {
-      const float m_new = fmaxf(m_ref, chunk_max(raw));
-      const float alpha = fast_exp2((m_ref - m_new) * c2);
-      l_part *= alpha;
+    //
+    // fp16 queries over an FP8 cache multiply each weight by its token's value
+    // scale before rounding it to fp16, whose range ends at 65504: there the
+    // reference is the exact running max of every chunk, so weights stay <= 1
+    // and weight * scale stays finite for any scale up to 65504.
+    float sum;
+    if constexpr (F16 && KV8) {
+      const float m_new = fmaxf(m_ref, chunk_max(sc));
+      if (__builtin_amdgcn_ballot_w64(m_new > m_ref)) {
+        const float alpha = fast_exp2((m_ref - m_new) * c2);
+        l_part *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      }
       m_ref = m_new;
-      sc = raw;
       sum = weights(sc);
+    } else {
+      if (t == 0) m_ref = fmaxf(m_ref, chunk_max(sc));
+      const f32x16 raw = sc;
+      sum = weights(sc);
+      if (__builtin_amdgcn_ballot_w64(!(sum <= kLazyRescaleDecW))) {
+        const float m_new = fmaxf(m_ref, chunk_max(raw));
+        const float alpha = fast_exp2((m_ref - m_new) * c2);
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        m_ref = m_new;
+        sc = raw;
+        sum = weights(sc);
+      }
     }
     l_part += sum;
     if constexpr (KV8) {

@@ -86,6 +86,11 @@ typedef enum {
 /*
  * attn_fwd - attention forward.
  *
+ * Defined by "FlashAttention：从 Safe Softmax 到分块计算" §1 (O = softmax(scale *
+ * Q K^T) V, row-wise softmax), computed by its §5/§7 tiled loop with the §3.1
+ * state and §3.2 merge; the mask of §5.2 (causal) and of "Attention 算子优化..."
+ * §二 (key padding); the row log-sum-exp of §8.
+ *
  * Computes, per (b, h) and valid query row i, O_i = sum_j P_ij V_j with
  * P_ij = exp(scale*q_i.k_j - LSE_i) over the visible keys j, and
  * LSE_i = ln(sum_j exp(scale*q_i.k_j)) (natural log).
@@ -122,6 +127,11 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype dtype);
 
 /*
  * attn_bwd - recompute-based attention backward.
+ *
+ * Defined by the AIInfra FlashAttention note on dpshk.com §2.3 (dV = P^T dO,
+ * dP = dO V^T, dS = P o (dP - rowsum(dP o P))) and "Attention 算子优化..." §四
+ * (P recomputed tile by tile from Q, K and the saved LSE instead of being
+ * stored); the scale factor of dQ and dK follows from S = scale * Q K^T.
  *
  * Given the forward's inputs q, k, v, its output o and lse, and the upstream
  * gradient dO, recomputes P tile by tile from q, k and lse and writes
@@ -208,6 +218,9 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
  * d is 64 or 128 as for attn_decode. HBM and LDS carry the 8-bit K/V; each
  * MFMA operand is widened to the 16-bit format on chip (exact), the scales are
  * applied in fp32 to the scores and to the weights before the V product.
+ * With fp16 queries the weights (each <= 1: the running max is exact there)
+ * times v_scale are rounded to fp16, so v_scale must stay below 65504; with
+ * bf16 queries the fp32 exponent range applies.
  */
 attn_status attn_decode_fp8kv(const void* q, const uint8_t* k8, const uint8_t* v8,
                               const float* k_scale, const float* v_scale, void* o, float* lse,

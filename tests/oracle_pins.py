@@ -40,7 +40,8 @@ def oracle_impl():
                                  fwd=lambda *a, **kw: A.attn_ref_fwd(*a, **kw),
                                  bwd=lambda *a, **kw: A.attn_ref_bwd(*a, **kw),
                                  decode=lambda *a, **kw: A.attn_ref_decode(*a, **kw),
-                                 e4m3=lambda *a, **kw: A.e4m3_decode(*a, **kw))
+                                 e4m3=lambda *a, **kw: A.e4m3_decode(*a, **kw),
+                                 dequant=lambda *a, **kw: A.dequant_fp8(*a, **kw))
 
 
 def _rng(seed):
@@ -581,8 +582,42 @@ def pin_e4m3_values(impl):
     assert np.all(same), f"E4M3 bytes {allb[~same][:8]} decode differently"
 
 
+def pin_dequant_fp8_values(impl):
+    """FP8 cache dequantisation ([OpOpt] §六: each cached token's K or V row is
+    stored as E4M3 bytes with one fp32 scale per token, value = byte value x
+    scale). Hand-worked values: three tokens (Nk = 3) of two columns (d = 2),
+    so a scale broadcast along the wrong axis cannot even line up, with a
+    different scale per token (0.5, 3, 10), none of them 1, so dividing
+    instead of multiplying or reusing one token's scale changes the result.
+    Bytes: 0x38 = 1, 0xC0 = -2, 0x40 = 2, 0x30 = 0.5, 0x7E = 448 (largest
+    finite), 0x01 = 2^-9 (smallest subnormal)."""
+    f = impl.dequant
+    x8 = np.array([[0x38, 0xC0], [0x40, 0x30], [0x7E, 0x01]], dtype=np.uint8)
+    sc = np.array([0.5, 3.0, 10.0])
+    want = np.array([[0.5, -1.0], [6.0, 1.5], [4480.0, 10.0 * 2.0 ** -9]])
+    got = f(x8, sc)
+    assert got.shape == want.shape, f"dequant shape {got.shape} vs {want.shape}"
+    assert np.array_equal(got, want), f"dequant values {got} vs {want}"
+    # A [B=1, H_kv=2, Nk=3, d=4] cache: the scale of (head g, token j) multiplies
+    # only that row. Row (g, j) holds the byte 0x38 + 8*j (1, 2, 4 for j = 0..2)
+    # in every column; scales 1 + g + 10 j (head 0: 1, 11, 21; head 1: 2, 12, 22).
+    x8 = np.zeros((1, 2, 3, 4), dtype=np.uint8)
+    sc = np.zeros((1, 2, 3))
+    for g in range(2):
+        for j in range(3):
+            x8[0, g, j, :] = 0x38 + 8 * j
+            sc[0, g, j] = 1 + g + 10 * j
+    want = np.array([[[[1.0] * 4, [22.0] * 4, [84.0] * 4],
+                      [[2.0] * 4, [24.0] * 4, [88.0] * 4]]])
+    got = f(x8, sc)
+    assert got.shape == want.shape and np.array_equal(got, want), f"dequant 4-d values {got}"
+    # torch tensors (the form the tests hand over) give the same values
+    got_t = f(torch.from_numpy(x8), torch.from_numpy(sc).to(torch.float32))
+    assert np.array_equal(got_t, want)
+
+
 DECODE_PINS = [pin_decode_is_last_forward_rows, pin_decode_torch_lower_right,
-               pin_decode_no_visible_key, pin_e4m3_values]
+               pin_decode_no_visible_key, pin_e4m3_values, pin_dequant_fp8_values]
 
 FWD_PINS = [pin_two_block_example, pin_merge_example, pin_safe_softmax_example,
             pin_hand_case_noncausal, pin_hand_case_causal, pin_hand_case_scaled,

@@ -7,24 +7,47 @@ Frobenius error for gradients:
   O:   fp32 inputs <= 1e-5, bf16 inputs <= 2e-2 (oracle fed the same bf16 values),
        fp16 inputs <= 2.5e-3 (the bf16 bar scaled by fp16's 2^-3 smaller unit
        roundoff: 11 vs 8 significand bits; O's error comes from rounding P and O)
-  LSE: fp32 <= 1e-5, bf16 and fp16 <= 1e-3 (the softmax statistics are kept in
-       fp32; LSE sits before any 16-bit rounding, so its error is that of fp32
-       score accumulation)
+  LSE: fp32 <= 1e-5; bf16 and fp16 <= 1e-4. LSE is computed before any 16-bit
+       rounding (the inputs are exact in fp32 and the statistics are fp32), so
+       its error is that of fp32 arithmetic: the score dot products (about
+       sqrt(d) * 2^-24 * scale * sum_c |q_c k_c|, ~5e-6 at d = 128 for N(0,1)
+       inputs, where scale * sum_c |q_c k_c| ~ 7.2), the exponent argument, the
+       fp32 sum of the weights (one rounding per 64-key tile) and the final
+       m * scale + ln l. These grow with the scores' magnitude, so the bar holds
+       for scores up to |S| = 8 (N(0,1) inputs with scale 1/sqrt(d) stay below
+       it: S is N(0,1) per entry); inputs with larger scores (the stress cases)
+       take it scaled by max|S| / 8 (lse_tol below).
   dQ, dK, dV: ||g - g_ref||_F / ||g_ref||_F <= 5e-2 per tensor for bf16, 1e-2
-       for fp16 (the bf16 bar scaled by 2^-3, rounded up). Where the oracle's
-       gradient is exactly zero (a single visible key: dS = P o (dP - D) with
-       dP = D), the relative error is undefined and the bar is max|g| <= 1e-5,
-       the size of the fp32 rounding left in dP - D.
+       for fp16 (the bf16 bar scaled by 2^-3, rounded up), and the same ratio
+       over every block of 64 rows (queries for dQ, keys for dK and dV) of
+       every head <= 1e-2 for bf16 and 2.5e-3 for fp16, so that an error
+       confined to one tile or one head cannot hide in the tensor-wide norm.
+       The gradients' error comes from rounding P, dS and the outputs to 16
+       bits (relative 2^-9 for bf16, about 1.1e-3 RMS after rounding), which
+       does not depend on where a block lies. Where the oracle's gradient is
+       exactly zero (a single visible key: dS = P o (dP - D) with dP = D), the
+       relative error is undefined and the bar is max|g| <= 1e-5, the size of
+       the fp32 rounding left in dP - D.
+
+Every comparison is appended, as one JSON line, to the file named by the
+environment variable PARITY_LOG when it is set: the error distribution over
+all cases that the AIInfra note (§3.1) asks to be gathered.
 """
 from __future__ import annotations
+
+import json
+import os
 
 import numpy as np
 import torch
 
 O_TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2.5e-3}
-LSE_TOL = {"f32": 1e-5, "bf16": 1e-3, "f16": 1e-3}
+LSE_TOL = {"f32": 1e-5, "bf16": 1e-4, "f16": 1e-4}
+LSE_S_REF = 8.0  # |S| up to which LSE_TOL holds unscaled
 GRAD_REL_FRO = 5e-2
 GRAD_TOL = {"bf16": GRAD_REL_FRO, "f16": 1e-2}
+GRAD_BLOCK_TOL = {"bf16": 1e-2, "f16": 2.5e-3}
+GRAD_BLOCK_ROWS = 64
 GRAD_ZERO_ABS = 1e-5
 
 
@@ -38,6 +61,33 @@ def to_np(t) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+def log(record: dict) -> None:
+    """Append one comparison record to $PARITY_LOG (if set)."""
+    path = os.environ.get("PARITY_LOG")
+    if not path:
+        return
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    with open(path, "a") as f:
+        f.write(json.dumps({"test": test, **record}) + "\n")
+
+
+def score_range(q, k, scale: float) -> float:
+    """max |S| = scale * max over (batch, head, i, j) of |q_i . k_j| (query head h
+    paired with K/V head h // (H // H_kv)), in fp64 on the CPU."""
+    qa, ka = to_np(q), to_np(k)
+    H, H_kv = qa.shape[1], ka.shape[1]
+    ka = np.repeat(ka, H // H_kv, axis=1)
+    return float(scale * np.max(np.abs(qa @ np.swapaxes(ka, -1, -2)))) if qa.size and ka.size else 0.0
+
+
+def lse_tol(dn: str, q=None, k=None, scale: float = 1.0) -> float:
+    """The LSE bar for these inputs: LSE_TOL, scaled by max|S| / 8 when the
+    scores reach beyond 8 in magnitude."""
+    if q is None:
+        return LSE_TOL[dn]
+    return LSE_TOL[dn] * max(1.0, score_range(q, k, scale) / LSE_S_REF)
+
+
 def metrics(got, ref) -> dict:
     g, r = to_np(got), to_np(ref)
     fin = np.isfinite(r)
@@ -48,11 +98,12 @@ def metrics(got, ref) -> dict:
     nrm = np.linalg.norm(gv) * np.linalg.norm(rv)
     return {"max_abs": float(diff.max()), "max_rel": float((diff / denom).max()),
             "cos": float(gv @ rv / nrm) if nrm > 0 else 1.0, "nonfinite": bad,
-            "inf_mismatch": int(np.sum(np.isfinite(g) != fin))}
+            "inf_mismatch": int(np.sum(np.isfinite(g) != fin)), "n": int(fin.sum())}
 
 
 def assert_close(got, ref, tol: float, what: str) -> dict:
     m = metrics(got, ref)
+    log({"what": what, "kind": "max_abs", "tol": tol, **m})
     assert m["nonfinite"] == 0, f"{what}: {m['nonfinite']} NaN/Inf where the oracle is finite ({m})"
     assert m["inf_mismatch"] == 0, f"{what}: finiteness pattern differs from the oracle ({m})"
     assert m["max_abs"] <= tol, f"{what}: max abs err {m['max_abs']:.3e} > {tol:.1e} ({m})"
@@ -62,3 +113,74 @@ def assert_close(got, ref, tol: float, what: str) -> dict:
 def rel_fro(got, ref) -> float:
     g, r = to_np(got), to_np(ref)
     return float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
+
+
+def check_grad(got, ref, tol: float, block_tol: float, what: str) -> dict:
+    """One gradient tensor [..., N, d] against the oracle's: finite, relative
+    Frobenius error <= tol over the tensor and <= block_tol over every block
+    of GRAD_BLOCK_ROWS rows of every leading index (head). Blocks whose exact
+    gradient is zero must be at most GRAD_ZERO_ABS in every entry."""
+    g, r = to_np(got), to_np(ref)
+    assert g.shape == r.shape, f"{what}: shape {g.shape} vs {r.shape}"
+    assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
+    rec = {"what": what, "kind": "grad", "tol": tol, "block_tol": block_tol}
+    if not np.any(r):
+        m = float(np.max(np.abs(g))) if g.size else 0.0
+        log({**rec, "zero_ref_max_abs": m})
+        assert m <= GRAD_ZERO_ABS, f"{what}: exact gradient is 0, got max|g|={m:.2e}"
+        return rec
+    e = rel_fro(g, r)
+    n, dd = r.shape[-2], r.shape[-1]
+    nb = (n + GRAD_BLOCK_ROWS - 1) // GRAD_BLOCK_ROWS
+    pad = nb * GRAD_BLOCK_ROWS - n
+    gp = np.pad(g.reshape(-1, n, dd), ((0, 0), (0, pad), (0, 0)))
+    rp = np.pad(r.reshape(-1, n, dd), ((0, 0), (0, pad), (0, 0)))
+    gb = gp.reshape(-1, nb, GRAD_BLOCK_ROWS * dd)
+    rb = rp.reshape(-1, nb, GRAD_BLOCK_ROWS * dd)
+    rn = np.linalg.norm(rb, axis=-1)
+    en = np.linalg.norm(gb - rb, axis=-1)
+    zero = rn == 0
+    zmax = float(np.max(np.abs(gb[zero]))) if zero.any() else 0.0
+    blk = np.where(zero, 0.0, en / np.where(zero, 1.0, rn))
+    worst = np.unravel_index(int(np.argmax(blk)), blk.shape)
+    rec.update({"rel_fro": e, "block_max": float(blk.max()), "block_median": float(np.median(blk[~zero])),
+                "worst_block": [int(i) for i in worst], "blocks": int((~zero).sum()),
+                "zero_blocks_max_abs": zmax, "max_abs": float(np.max(np.abs(g - r)))})
+    log(rec)
+    assert e <= tol, f"{what}: rel Frobenius err {e:.3e} > {tol}"
+    assert float(blk.max()) <= block_tol, (
+        f"{what}: rel Frobenius err {float(blk.max()):.3e} > {block_tol} in the {GRAD_BLOCK_ROWS}-row "
+        f"block {worst[-1]} of head {worst[0]} (tensor-wide {e:.3e})")
+    assert zmax <= GRAD_ZERO_ABS, f"{what}: {zmax:.2e} where the exact gradient block is 0"
+    return rec
+
+
+def check_grads(got, ref, what: str, dn: str | None = None) -> None:
+    """dQ, dK, dV against the oracle with the bars of their dtype."""
+    if dn is None:
+        dn = dtype_name(got[0]) if isinstance(got[0], torch.Tensor) else "bf16"
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        check_grad(g, r, GRAD_TOL[dn], GRAD_BLOCK_TOL[dn], f"{what} {name}")
+
+
+def oracle_fwd_threads(q, k, v, scale: float, causal: bool, seqlens=None, workers: int = 4):
+    """oracle.attn_ref_fwd evaluated head by head on a few threads (each call is
+    the unchanged per-head oracle; BLAS and numpy release the GIL), for the
+    full-size workloads. Returns (O, LSE) fp64."""
+    import concurrent.futures
+    import oracle
+    qn, kn, vn = to_np(q), to_np(k), to_np(v)
+    B, H, N, _ = qn.shape
+    H_kv = kn.shape[1]
+    lens = [N] * B if seqlens is None else [int(min(max(int(L), 0), N)) for L in seqlens.tolist()]
+    o = np.zeros(qn.shape[:3] + (vn.shape[-1],))
+    lse = np.zeros(qn.shape[:3])
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        g = oracle.kv_head(h, H, H_kv)
+        o[b, h], lse[b, h] = oracle.attn_ref_head(qn[b, h], kn[b, g], vn[b, g], scale, causal, lens[b])
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, range(B * H)))
+    return o, lse

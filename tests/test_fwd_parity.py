@@ -14,7 +14,7 @@ import torch
 import exact_attention_24_amd as ea
 import oracle
 from attn_inputs import WORKLOADS, make_inputs, make_workload_inputs
-from tests.parity import LSE_TOL, O_TOL, assert_close, dtype_name, to_np
+from tests.parity import LSE_TOL, O_TOL, assert_close, dtype_name, lse_tol, oracle_fwd_threads, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -34,7 +34,7 @@ def check_full(x, scale, causal, tag):
     ro, rl = oracle.attn_ref_fwd(q, k, v, scale, causal, sl)
     dn = dtype_name(q)
     assert_close(o, ro, O_TOL[dn], f"{tag} O")
-    assert_close(lse, rl, LSE_TOL[dn], f"{tag} LSE")
+    assert_close(lse, rl, lse_tol(dn, q, k, scale), f"{tag} LSE")
     # padded rows exactly zero, LSE exactly -inf
     if sl is not None:
         for b, L in enumerate(sl.tolist()):
@@ -63,7 +63,9 @@ def test_hand_case(dtype, d, causal):
     tol = {torch.float32: 1e-5, torch.bfloat16: 2 ** -6 + 2 ** -9 * 8,
            torch.float16: 2 ** -9 + 2 ** -11 * 8}[dtype]
     assert_close(o, ro, tol, "hand O")
-    assert_close(lse, rl, LSE_TOL[dtype_name(q)], "hand LSE")
+    # the inputs are small integers, exact in every format, and LSE never sees a
+    # 16-bit rounding: fp32 statistics reach 1e-5 whatever the input format
+    assert_close(lse, rl, 1e-5, "hand LSE")
     assert torch.all(o[..., 2:] == 0)
     if causal:
         assert torch.equal(o[0, 0, 0, :2], V[0].to(dtype)), "causal row 0 must be V_0 exactly"
@@ -94,7 +96,7 @@ def test_two_block_example(dtype):
     o, lse = run_fwd(q, k, v, 1.0)
     l = 2 * math.exp(-2) + math.exp(-1) + 1
     assert abs(math.exp(float(lse[0, 0, 0]) - 3.0) - 1.638) <= 1e-3  # the page's printed value
-    assert abs(float(lse[0, 0, 0]) - (3 + math.log(l))) <= LSE_TOL[dtype_name(q)]
+    assert abs(float(lse[0, 0, 0]) - (3 + math.log(l))) <= 1e-5  # exact inputs, fp32 statistics
     want = (0.5 * math.exp(-2) + 1.0 * math.exp(-1) + 1.5 + 2.0 * math.exp(-2)) / l
     # bf16: O ~ 1.35, half an ulp in [1, 2) is 2^-8, plus 2^-9 * max|V| = 2^-8;
     # fp16: 2^-11 + 2^-11 * max|V|
@@ -116,7 +118,7 @@ def test_merge_example(dtype):
     u = math.exp(-1) * (10 * math.exp(-1) + 20) + 30
     tol = 1e-5 if dtype == torch.float32 else 2e-2
     assert abs(float(o[0, 0, 0, 0]) - f * u / l) <= tol
-    assert abs(float(lse[0, 0, 0]) - (3 + math.log(l))) <= LSE_TOL[dtype_name(q)]
+    assert abs(float(lse[0, 0, 0]) - (3 + math.log(l))) <= 1e-5  # exact inputs, fp32 statistics
 
 
 # ----------------------------------------------- small shapes, full comparison
@@ -162,36 +164,27 @@ def test_varlen_length_order(causal, heads):
     check_full(x, 1 / math.sqrt(d), causal, "length-ordered varlen")
 
 
-# ------------------------------------------------ full workloads, sampled rows
+# ------------------------------------------------ full workloads, every output
 
 FWD_WORKLOADS = [n for n, w in WORKLOADS.items() if w.Nq is None]  # decode has its own test
 
 
-def _sample_rows(N, L, rng, k=40):
-    base = {0, 1, 31, 32, 63, 64, 127, 128, N - 1, max(L - 1, 0), min(L, N - 1)}
-    base |= set(rng.integers(0, N, size=k).tolist())
-    return sorted(r for r in base if 0 <= r < N)
-
-
 @pytest.mark.parametrize("name", FWD_WORKLOADS)
-def test_workload_sampled(name):
+def test_workload_full(name):
     """Each workload at its full size, in the launch configuration the benchmark
-    times; the oracle evaluates sampled rows of sampled heads one by one."""
+    times: every O and LSE entry of every head against the oracle ([AIInfra]
+    §3.1's random comparison, whole tensors); padded rows exactly 0 / -inf."""
     w = WORKLOADS[name]
     x = make_workload_inputs(w)
     q, k, v, sl = x["q"], x["k"], x["v"], x["seqlens"]
+    print(f"workload {name}: GPU forward", flush=True)
     o, lse = run_fwd(q, k, v, w.scale, w.causal, sl)
     assert torch.isfinite(o).all(), "non-finite output"
-    rng = np.random.default_rng(w.seed)
-    heads = {(0, 0), (w.B - 1, w.H - 1)} | {(int(rng.integers(w.B)), int(rng.integers(w.H)))
-                                             for _ in range(3)}
+    print(f"workload {name}: oracle over {w.B * w.H} heads", flush=True)
+    ro, rl = oracle_fwd_threads(q, k, v, w.scale, w.causal, sl)
     dn = dtype_name(q)
-    for b, h in sorted(heads):
-        L = w.N if sl is None else int(sl[b])
-        rows = _sample_rows(w.N, L, rng)
-        ro, rl = oracle.attn_ref_rows(q, k, v, b, h, rows, w.scale, w.causal, sl)
-        assert_close(o[b, h, rows], ro, O_TOL[dn], f"{name} O (b={b},h={h})")
-        assert_close(lse[b, h, rows], rl, LSE_TOL[dn], f"{name} LSE (b={b},h={h})")
+    assert_close(o, ro, O_TOL[dn], f"{name} O")
+    assert_close(lse, rl, LSE_TOL[dn], f"{name} LSE")
     if sl is not None:
         for b, L in enumerate(sl.tolist()):
             assert torch.all(o[b, :, L:] == 0) and torch.all(torch.isneginf(lse[b, :, L:]))
@@ -229,7 +222,7 @@ def test_f16_large_values(d):
     o, lse = run_fwd(x["q"], x["k"], x["v"], 1 / math.sqrt(d), True)
     ro, rl = oracle.attn_ref_fwd(x["q"], x["k"], x["v"], 1 / math.sqrt(d), True)
     assert_close(o, ro, O_TOL["f16"] * 64, "f16 large values O")
-    assert_close(lse, rl, LSE_TOL["f16"], "f16 large values LSE")
+    assert_close(lse, rl, lse_tol("f16", x["q"], x["k"], 1 / math.sqrt(d)), "f16 large values LSE")
 
 
 def rising_scores(B, H, N, d, dtype, step, seed):
@@ -258,7 +251,7 @@ def test_rising_scores_move_the_reference(causal, dtype):
     ro, rl = oracle.attn_ref_fwd(x["q"], x["k"], x["v"], 1.0, causal)
     dn = dtype_name(x["q"])
     assert_close(o, ro, O_TOL[dn], "rising scores O")
-    assert_close(lse, rl, LSE_TOL[dn], "rising scores LSE")
+    assert_close(lse, rl, lse_tol(dn, x["q"], x["k"], 1.0), "rising scores LSE")
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])

@@ -162,7 +162,7 @@ def test_unmutated_backward_copy_passes():
     """The mutant factory with no mutation passes every pin (the harness is sound)."""
     impl = types.SimpleNamespace(head=A.attn_ref_head, bwd_head=_bwd_factory("none"),
                                  fwd=A.attn_ref_fwd, bwd=A.attn_ref_bwd, decode=A.attn_ref_decode,
-                                 e4m3=A.e4m3_decode)
+                                 e4m3=A.e4m3_decode, dequant=A.dequant_fp8)
     assert _run_pins(impl, ALL_PINS) == []
 
 
@@ -224,7 +224,8 @@ def _decode_factory(offset_kind):
 @pytest.mark.parametrize("kind", ["top_left", "off_by_one"])
 def test_decode_position_mutant_is_caught(kind):
     impl = types.SimpleNamespace(head=A.attn_ref_head, fwd=A.attn_ref_fwd,
-                                 decode=_decode_factory(kind), e4m3=A.e4m3_decode)
+                                 decode=_decode_factory(kind), e4m3=A.e4m3_decode,
+                                 dequant=A.dequant_fp8)
     assert _run_pins(impl, DECODE_PINS), f"decode mutant {kind} passed every decode pin"
 
 
@@ -245,5 +246,40 @@ def _e4m3_no_subnormals(byte_values):
 @pytest.mark.parametrize("fn", [_e4m3_bias8, _e4m3_no_subnormals], ids=["bias8", "no_subnormals"])
 def test_e4m3_mutant_is_caught(fn):
     impl = types.SimpleNamespace(head=A.attn_ref_head, fwd=A.attn_ref_fwd, decode=A.attn_ref_decode,
-                                 e4m3=fn)
+                                 e4m3=fn, dequant=A.dequant_fp8)
     assert _run_pins(impl, DECODE_PINS), "E4M3 decoder mutant passed every pin"
+
+
+# ---- FP8 dequantisation mutants: the per-token scale applied wrongly
+
+def _dequant_divide(x8, scale):
+    """Divides by the scale instead of multiplying."""
+    return A.e4m3_decode(np.asarray(x8)) / np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def _dequant_column_axis(x8, scale):
+    """Broadcasts the per-token scale along the columns instead of the tokens."""
+    return A.e4m3_decode(np.asarray(x8)) * np.asarray(scale, dtype=np.float64)[..., None, :]
+
+
+def _dequant_first_token(x8, scale):
+    """Uses the first token's scale for every token of a head."""
+    s = np.asarray(scale, dtype=np.float64)
+    return A.e4m3_decode(np.asarray(x8)) * s[..., :1, None]
+
+
+def _dequant_flat_scale(x8, scale):
+    """Indexes the scales by token only, ignoring the head (head 0's scales everywhere)."""
+    s = np.asarray(scale, dtype=np.float64)
+    if s.ndim >= 2:
+        s = np.broadcast_to(s[..., :1, :], s.shape)
+    return A.e4m3_decode(np.asarray(x8)) * s[..., None]
+
+
+@pytest.mark.parametrize("fn", [_dequant_divide, _dequant_column_axis, _dequant_first_token,
+                                _dequant_flat_scale],
+                         ids=["divide", "column_axis", "first_token", "flat_scale"])
+def test_dequant_mutant_is_caught(fn):
+    impl = types.SimpleNamespace(head=A.attn_ref_head, fwd=A.attn_ref_fwd, decode=A.attn_ref_decode,
+                                 e4m3=A.e4m3_decode, dequant=fn)
+    assert _run_pins(impl, DECODE_PINS), "dequantisation mutant passed every pin"
