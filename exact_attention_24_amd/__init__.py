@@ -15,7 +15,8 @@ import os
 import pathlib
 from typing import Optional
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_fp8kv",
+__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_workspace_bytes", "attn_decode",
+           "attn_decode_fp8kv",
            "attn_decode_workspace_bytes", "attn_status_string",
            "AttnError", "lib", "LIB_PATH", "DTYPE_F32", "DTYPE_BF16", "DTYPE_F16",
            "EXPORTED_SYMBOLS"]
@@ -27,7 +28,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_F16 = 2
 # Every function include/attn.h declares.
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_gqa", "attn_bwd", "attn_bwd_gqa",
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_gqa", "attn_bwd", "attn_bwd_gqa", "attn_bwd_noalloc",
                     "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_fp8kv",
                     "attn_decode_workspace_bytes", "attn_status_string", "attn_last_error")
 
@@ -63,6 +64,9 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     L.attn_bwd_gqa.restype = i32
+    L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
+    L.attn_bwd_noalloc.restype = i32
     L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp,
@@ -226,6 +230,32 @@ def attn_bwd(q, k, v, o, do, lse, *, scale: Optional[float] = None, causal: bool
     else:
         st = lib().attn_bwd_gqa(*ptrs, B, H, H_kv, N, d, *tail)
         _check(st, "attn_bwd_gqa")
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, do, lse, *, scale: Optional[float] = None, causal: bool = False,
+                     seqlens=None, dq, dk, dv):
+    """attn_bwd into caller-provided dq, dk, dv with no workspace: the library's
+    static device scratch holds the backward's per-row statistics (at most
+    2^21 = B*H*N query rows). Nothing is allocated, so it can run where
+    allocation is not allowed (under graph capture, for instance). Calls that
+    may overlap on one GPU share that scratch and must not run concurrently."""
+    import torch
+    B, H, N, d = q.shape
+    dev = q.device
+    H_kv = _kv_heads(q, k)
+    for name, t in (("q", q), ("o", o), ("do", do), ("dq", dq)):
+        _check_tensor(name, t, (B, H, N, d), q.dtype, dev)
+    for name, t in (("k", k), ("v", v), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, (B, H_kv, N, d), q.dtype, dev)
+    _check_tensor("lse", lse, (B, H, N), torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                B, H, H_kv, N, d, _dtype_code(q), float(scale), int(bool(causal)),
+                                _seqlens_ptr(seqlens, B, dev), _stream_handle(dev))
+    _check(st, "attn_bwd_noalloc")
     return dq, dk, dv
 
 

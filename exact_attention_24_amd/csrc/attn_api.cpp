@@ -9,7 +9,18 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "attn_kernels.h"
+
+// Static device scratch of attn_bwd_noalloc: the backward workspace for
+// callers that cannot allocate. Each GPU holds its own copy of the array; in
+// host code `scratch` is only a host-side stand-in for it, so kernels and
+// copies get the device address that hipGetSymbolAddress returns, looked up
+// once per device with that device current (scratch_ptr below).
+static_assert(2 * ((ATTN_NOALLOC_MAX_ROWS * 4 + 255) / 256 * 256) <= (long long)ATTN_NOALLOC_SCRATCH_BYTES,
+              "the scratch holds both fp32 sections for the largest row count");
+static __device__ __attribute__((aligned(256))) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -99,6 +110,29 @@ attn_status check_decode(int B, int H, int H_kv, int Nq, int Nk, int d, attn_dty
 size_t attn_bwd_section_bytes(int B, int H, int N) {
   const size_t rows = (size_t)B * H * N;
   return ((rows * sizeof(float) + 255) / 256) * 256;
+}
+
+// Device addresses of the static scratch array (below), one per device.
+constexpr int kMaxDevices = 256;
+void* scratch_dev[kMaxDevices];
+std::mutex scratch_mu;
+
+// Device address of the current device's scratch array (looked up on first use).
+hipError_t scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -199,6 +233,34 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      float scale, int causal, const int32_t* seqlens, attn_stream_t stream) {
   return attn_bwd_gqa(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d,
                       dtype, scale, causal, seqlens, stream);
+}
+
+attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                             const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                             int H, int H_kv, int N, int d, attn_dtype dtype, float scale,
+                             int causal, const int32_t* seqlens, attn_stream_t stream) {
+  // Every size check comes before the scratch lookup, so a rejected call makes
+  // no HIP call at all.
+  attn_status st = check_sizes(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if ((long long)B * H * N > ATTN_NOALLOC_MAX_ROWS) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "attn_bwd_noalloc: B*H*N = %lld query rows exceed the static scratch's limit of %lld",
+             (long long)B * H * N, (long long)ATTN_NOALLOC_MAX_ROWS);
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (dtype == ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  hipError_t e = scratch_ptr(&ws);
+  if (e != hipSuccess) {
+    record_hip_error(e, "attn_bwd_noalloc scratch lookup");
+    return ATTN_ERR_HIP;
+  }
+  return attn_bwd_gqa(q, k, v, o, dO, lse, dq, dk, dv, ws, ATTN_NOALLOC_SCRATCH_BYTES, B, H, H_kv,
+                      N, d, dtype, scale, causal, seqlens, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d,

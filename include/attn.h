@@ -36,7 +36,8 @@
  *    ((b*H + h)*N + i)*d + c). Q, K, V, O, dO, dQ, dK, dV share one shape.
  *  - All tensor pointers are DEVICE pointers. The caller allocates and owns
  *    every buffer; the library allocates nothing and keeps no state between
- *    calls. Buffers must be 16-byte aligned.
+ *    calls (the one exception is attn_bwd_noalloc's static device scratch).
+ *    Buffers must be 16-byte aligned.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    null stream). No entry point synchronises the host.
  *  - Argument errors are detected on the host before anything is launched and
@@ -165,6 +166,36 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, int B, int H, int H_kv, int N,
                          int d, attn_dtype dtype, float scale, int causal,
                          const int32_t* seqlens, attn_stream_t stream);
+
+/*
+ * attn_bwd_noalloc - attn_bwd_gqa without a workspace argument, for callers
+ * that cannot allocate device memory at all (code under HIP graph capture,
+ * tight serving or training loops, harnesses that forbid allocation).
+ *
+ * The workspace of attn_bwd_gqa (-D and LSE * log2(e), fp32 [B,H,N] each)
+ * lives instead in a static device array of ATTN_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on each GPU it runs on until the process ends; its
+ * device address is looked up once per device (on the first call with that
+ * device current) and kept. The call allocates nothing, neither directly nor
+ * through any library routine. Every other argument, output and error is as
+ * for attn_bwd_gqa (H_kv = H is plain attn_bwd), and the results are
+ * bit-identical to it: the same kernels run.
+ *
+ * Limit: B * H * N <= ATTN_NOALLOC_MAX_ROWS (2^21 query rows, e.g. B=2, H=32,
+ * N=32768); larger sizes return ATTN_ERR_UNSUPPORTED before anything is
+ * launched (attn_last_error() names the limit).
+ * Concurrency: every call on one GPU uses that GPU's one scratch array. Calls
+ * on the same stream are ordered and safe; calls that may overlap on one GPU
+ * (different streams, or different host threads without ordering) race on the
+ * scratch and give undefined results. The scratch needs no clearing: each
+ * call writes every entry it reads before reading it.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+#define ATTN_NOALLOC_MAX_ROWS ((long long)1 << 21)
+attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                             const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                             int B, int H, int H_kv, int N, int d, attn_dtype dtype, float scale,
+                             int causal, const int32_t* seqlens, attn_stream_t stream);
 
 /*
  * attn_decode_workspace_bytes - device workspace attn_decode needs for these

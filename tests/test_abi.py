@@ -208,3 +208,30 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ea, "LIB_PATH", tmp_path / "nope.so")
     with pytest.raises(RuntimeError, match="not found"):
         ea.lib()
+
+
+def bwd_noalloc(L, **kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, H=4, H_kv=2, N=64, d=64,
+             dtype=1, scale=0.125, causal=0, seqlens=0)
+    a.update(kw)
+    return L.attn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                              a["dv"], a["B"], a["H"], a["H_kv"], a["N"], a["d"], a["dtype"],
+                              a["scale"], a["causal"], a["seqlens"], 0)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=0), INVALID), (dict(dv=0), INVALID), (dict(lse=0), INVALID), (dict(B=0), INVALID),
+    (dict(H_kv=3), INVALID), (dict(d=96), UNSUPPORTED), (dict(scale=0.0), INVALID),
+    (dict(dtype=0), UNSUPPORTED), (dict(dtype=9), INVALID),
+    # 2^21 query rows is the static scratch's limit: one more row is refused
+    (dict(B=1, H=64, H_kv=64, N=32769), UNSUPPORTED), (dict(B=2, H=32, H_kv=32, N=32769), UNSUPPORTED),
+])
+@cpu_only
+def test_bwd_noalloc_rejects_bad_arguments(L, kw, want):
+    assert bwd_noalloc(L, **kw) == want
+
+
+@cpu_only
+def test_bwd_noalloc_names_its_limit(L):
+    assert bwd_noalloc(L, B=4, H=32, H_kv=32, N=16385) == UNSUPPORTED
+    assert b"2097152" in L.attn_last_error()
