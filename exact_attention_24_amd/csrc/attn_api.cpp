@@ -56,25 +56,27 @@ attn_status check_heads(int H, int H_kv) {
 
 // Split plan of the decode: `splits` key ranges of `chunk_keys` keys (a
 // multiple of 32) per (batch, K/V head). 0 requested splits picks enough for
-// one resident round of workgroups on 256 CUs (at most three per CU: the split
-// kernel's 42-48 KiB of LDS). More, shorter workgroups were measured slower
-// (each pays its start-up latency again; B=8, 8 K/V heads, 8192 keys: 32
-// splits 52.7 us, 12 splits 49.6 us for bf16, 53.7 -> 46.9 us for FP8 K/V).
+// one resident round of workgroups on 256 CUs (three per CU for the 16-bit
+// split kernel's 48 KiB of LDS, four for the FP8 kernel's 34 KiB). More,
+// shorter workgroups were measured slower (each pays its start-up latency
+// again; B=8, 8 K/V heads, 8192 keys: 32 splits 52.7 us, 12 splits 49.6 us
+// for bf16, 53.7 -> 46.9 us for FP8 K/V).
 struct DecodePlan {
   int splits, chunk_keys, col_groups;
 };
 // Automatic split count: about `target` workgroups. Measured on the B=8,
-// H=64, H_kv=8, Nk=8192 workloads: one-wave workgroups over a 16-bit cache do
-// best at ~512 (fewer splits also shrink the merge), FP8 caches and two-wave
-// workgroups at ~768. The FP8 plan never has fewer splits, so it sizes the
-// workspace for both.
+// H=64, H_kv=8, Nk=8192 workloads with the caches in HBM only (each call timed
+// after a 512 MiB read): one-wave workgroups over a 16-bit cache do best at
+// ~512 (fewer splits also shrink the merge), two-wave workgroups at ~768, FP8
+// caches (smaller workgroups: a 32 KiB ring) at ~1024. The FP8 plan never has
+// fewer splits, so it sizes the workspace for all.
 DecodePlan decode_plan(int B, int H, int H_kv, int Nq, int Nk, int num_splits, bool kv8) {
   DecodePlan p;
   p.col_groups = ((H / H_kv) * Nq + 31) / 32;
   long long want = num_splits;
   if (want <= 0) {
     const int nw = attn::decode_waves(p.col_groups);
-    const long long target = (!kv8 && nw == 1) ? 512 : 768;
+    const long long target = kv8 ? 1024 : (nw == 1 ? 512 : 768);
     const long long units = (long long)B * H_kv * (p.col_groups / nw);
     want = (target + units - 1) / units;
   }

@@ -100,9 +100,11 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int LPC = 2 * TileDma<DD, BN, NW>::ITER + (KV8 ? 2 : 0);  // loads per chunk and wave
   // Ring of NST chunk stages, NST - 1 chunks in flight. An FP8 chunk is half
-  // the bytes of a 16-bit one, so its ring is deeper: both keep about 32 KiB
-  // per wave in flight (a split is bound by its loads' latency, not by HBM).
-  constexpr int NST = KV8 ? 5 : 3;
+  // the bytes of a 16-bit one, so its ring is one stage deeper. Measured on
+  // the B=8, 64:8-head, 8192-position workloads with the caches in HBM only:
+  // 3 stages (16-bit) and 4 (FP8) with the split counts chosen in the host
+  // code were the best of ring depths 2-7 and 256-1536 workgroups.
+  constexpr int NST = KV8 ? 4 : 3;
   __shared__ __attribute__((aligned(1024))) char kr_[NST][TILE], vr_[NST][TILE];
   // FP8 only: per-stage token scales (64 floats fetched, the first 32 used).
   // K and V operands are widened in registers from the FP8 tiles.

@@ -223,9 +223,9 @@ size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d
  *            every valid key. A query that sees no key gets O = 0, LSE = -inf.
  *  num_splits  key-range splits per (batch, K/V head); 0 picks a count
  *            that gives about 512 workgroups for one-wave workgroups over a
- *            16-bit cache and about 768 otherwise (FP8 cache, or query
- *            columns in pairs of 32-column blocks, whose workgroups hold two
- *            waves). Results do not depend on it beyond rounding.
+ *            16-bit cache, about 768 for query columns in pairs of 32-column
+ *            blocks (two-wave workgroups) and about 1024 over an FP8 cache.
+ *            Results do not depend on it beyond rounding.
  *  workspace device buffer of attn_decode_workspace_bytes(...) bytes, 256-byte
  *            aligned; contents on entry are ignored.
  *
