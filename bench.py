@@ -334,32 +334,35 @@ def sweep_inputs(torch, w, dev):
     return {"q": q, "k": k, "v": v, "seqlens": None}
 
 
-def extras(torch, ea, timer, steps, warmup, log, parts=("suite", "sweep", "bwd", "decode")):
+def extras(torch, ea, timer, steps, warmup, log, parts=("suite", "sweep", "bwd", "decode"),
+           only=None):
     """Every other forward workload, the context sweep, the backward and the
-    decode workloads (one dict each); ``parts`` selects which."""
+    decode workloads (one dict each); ``parts`` selects which and ``only``, if
+    given, keeps the one workload of that name."""
     from attn_inputs import WORKLOADS, Workload
+    pick = lambda names: [n for n in names if only is None or n == only]
     out = {}
     if "suite" in parts:
         out["suite"] = {}
-        for name in SUITE_WORKLOADS:
+        for name in pick(SUITE_WORKLOADS):
             log(f"suite {name}")
             out["suite"][name] = fwd_case(torch, ea, timer, WORKLOADS[name], steps, warmup)
     if "sweep" in parts:
         out["sweep"] = {}
-        for n in SWEEP_N:
+        for n in [n for n in SWEEP_N if only is None or only == f"sweep_causal_bf16_b2_h32_n{n}_d128"]:
             w = Workload(f"sweep_causal_bf16_b2_h32_n{n}_d128", 2, 32, n, 128, "bf16", True, 2000 + n)
             log(f"sweep N={n}")
             out["sweep"][w.name] = fwd_case(torch, ea, timer, w, steps, warmup,
                                             x=sweep_inputs(torch, w, "cuda:0"))
     if "bwd" in parts:
         out["bwd_suite"] = {}
-        for name in BWD_WORKLOADS:
+        for name in pick(BWD_WORKLOADS):
             log(f"backward {name}")
             out["bwd_suite"][name] = bwd_case(torch, ea, timer, WORKLOADS[name], max(steps // 2, 5),
                                               max(warmup // 2, 2))
     if "decode" in parts:
         out["decode"] = {}
-        for name in DECODE_WORKLOADS:
+        for name in pick(DECODE_WORKLOADS):
             log(f"decode {name}")
             out["decode"][name] = decode_case(torch, ea, timer, name, steps, warmup)
     return out
@@ -406,6 +409,9 @@ def main():
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the traffic figure; gemm: a "
                          "library bf16 GEMM on random and on zero operands, the dense-MFMA rate "
                          "reachable under this GPU's power limit (context only)")
+    ap.add_argument("--only", default=None, metavar="WORKLOAD",
+                    help="with --mode suite / sweep / bwd / decode: run only the workload of this "
+                         "name (for profiling one kernel instantiation)")
     ap.add_argument("--values", choices=["random", "zeros"], default="random",
                     help="'zeros' runs the headline launches on all-zero Q, K, V, a diagnostic of "
                          "data-dependent power (the clock the chip holds under MFMA load depends "
@@ -433,7 +439,7 @@ def main():
     torch.cuda.set_device(dev)
     if args.mode in ("suite", "sweep", "bwd", "decode"):
         part = extras(torch, ea, Timer(torch, dev, args.settle_ms), args.steps, args.warmup, log,
-                      parts=(args.mode,))
+                      parts=(args.mode,), only=args.only)
         print(json.dumps({"mode": args.mode, **part}), flush=True)
         return
     w = WORKLOADS[WORKLOAD]
