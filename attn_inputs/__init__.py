@@ -23,7 +23,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "draw_seqlens", "workload", "fp8_cache"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "draw_seqlens", "workload", "fp8_cache",
+           "fp8_head"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -155,6 +156,25 @@ def fp8_cache(x: torch.Tensor):
     amax = xf.abs().amax(dim=-1)
     scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
     q8 = (xf / scale[..., None]).to(torch.float8_e4m3fn)
+    return q8.view(torch.uint8).contiguous(), scale.contiguous()
+
+
+def fp8_head(x: torch.Tensor, valid_len=None):
+    """Store a tensor [B, H, N, d] as FP8 with one fp32 scale per (batch, head):
+    amax over the head's valid rows / 448, the head divided by it and rounded
+    to E4M3 by torch's conversion. valid_len (int32 [B] or None) limits the
+    amax to rows < L_b; rows at or past it are quantised like the others (a
+    caller that wants them poisoned overwrites them). Returns (uint8 bytes,
+    fp32 scales [B, H]). Heads of zeros get scale 1."""
+    xf = x.float()
+    if valid_len is not None:
+        rows = torch.arange(x.shape[2])[None, :] < valid_len.to(torch.int64)[:, None]
+        xf_valid = xf * rows[:, None, :, None]
+    else:
+        xf_valid = xf
+    amax = xf_valid.abs().amax(dim=(-2, -1))
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q8 = (xf / scale[..., None, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
     return q8.view(torch.uint8).contiguous(), scale.contiguous()
 
 

@@ -40,6 +40,7 @@ import time
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 WORKLOAD = "causal_bf16_b2_h32_n4096_d128"
 METRIC = "attention fwd TFLOPS (and % of bf16 MFMA peak) at B=2,H=32,N=4096,d=128 causal"
@@ -245,6 +246,37 @@ def fwd_case(torch, ea, timer, w, steps, warmup, x=None, dev="cuda:0"):
             "peak_tflops": peak, "flop_convention": "4*H*sum_b L_b^2*d, halved if causal"}
 
 
+FP8_WORKLOADS = {"fp8_causal_b2_h32_n4096_d128": (2, 32, 4096, True, 4242)}
+
+
+def fwd8_case(torch, ea, timer, name, steps, warmup, dev="cuda:0"):
+    """The FP8 forward (attn_fwd_fp8) on the headline shape: seeded N(0,1)
+    inputs quantised to E4M3, Q with one scale per token, K and V with one per
+    (batch, head). FLOPs as for the 16-bit forward; the fraction is of the
+    dense FP8 MFMA peak, with the bf16 peak's fraction alongside."""
+    from attn_inputs import fp8_cache, fp8_head, make_inputs
+    B, H, N, causal, seed = FP8_WORKLOADS[name]
+    x = make_inputs(B, H, N, 128, torch.float32, seed=seed)
+    q8, qs = fp8_cache(x["q"])
+    k8, ks = fp8_head(x["k"])
+    v8, vs = fp8_head(x["v"])
+    q8, qs, k8, ks, v8, vs = (t.to(dev) for t in (q8, qs, k8, ks, v8, vs))
+    o = torch.empty((B, H, N, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    flops = fwd_flops(B, H, N, 128, causal)
+    fn = lambda: ea.attn_fwd_fp8(q8, k8, v8, qs, ks, vs, causal=causal, out=o, lse=lse)
+    wall_ms, ev_ms = timer.region(fn, steps, warmup)
+    med, p90 = stats(timer.cold(fn, steps))
+    return {"B": B, "H": H, "N": N, "d": 128, "dtype": "fp8 e4m3 (O bf16)", "causal": causal,
+            "gflop": round(flops / 1e9, 3), "ms_back_to_back": round(ev_ms, 4),
+            "ms_median_cold": round(med, 4), "ms_p90_cold": round(p90, 4),
+            "tflops_back_to_back": round(rate(flops, ev_ms), 1),
+            "tflops_median_cold": round(rate(flops, med), 1),
+            "frac_of_fp8_peak": round(rate(flops, ev_ms) / PEAK_FP8_TFLOPS, 4),
+            "frac_of_bf16_peak": round(rate(flops, ev_ms) / PEAK_BF16_TFLOPS, 4),
+            "peak_tflops": PEAK_FP8_TFLOPS, "flop_convention": "4*B*H*N^2*d, halved if causal"}
+
+
 def bwd_case(torch, ea, timer, w, steps, warmup, dev="cuda:0"):
     """The recompute backward (delta, dK/dV and dQ kernels) on a workload with
     dO, with O and LSE from one forward pass. FLOPs follow the 5-GEMM
@@ -347,6 +379,9 @@ def extras(torch, ea, timer, steps, warmup, log, parts=("suite", "sweep", "bwd",
         for name in pick(SUITE_WORKLOADS):
             log(f"suite {name}")
             out["suite"][name] = fwd_case(torch, ea, timer, WORKLOADS[name], steps, warmup)
+        for name in pick(list(FP8_WORKLOADS)):
+            log(f"suite {name}")
+            out["suite"][name] = fwd8_case(torch, ea, timer, name, steps, warmup)
     if "sweep" in parts:
         out["sweep"] = {}
         for n in [n for n in SWEEP_N if only is None or only == f"sweep_causal_bf16_b2_h32_n{n}_d128"]:

@@ -15,7 +15,7 @@ import os
 import pathlib
 from typing import Optional
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_workspace_bytes", "attn_decode",
+__all__ = ["attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_workspace_bytes", "attn_decode",
            "attn_decode_fp8kv",
            "attn_decode_workspace_bytes", "attn_status_string",
            "AttnError", "lib", "LIB_PATH", "DTYPE_F32", "DTYPE_BF16", "DTYPE_F16",
@@ -28,7 +28,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_F16 = 2
 # Every function include/attn.h declares.
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_gqa", "attn_bwd", "attn_bwd_gqa", "attn_bwd_noalloc",
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_gqa", "attn_fwd_fp8", "attn_bwd", "attn_bwd_gqa", "attn_bwd_noalloc",
                     "attn_bwd_workspace_bytes", "attn_decode", "attn_decode_fp8kv",
                     "attn_decode_workspace_bytes", "attn_status_string", "attn_last_error")
 
@@ -56,6 +56,9 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = i32
     L.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     L.attn_fwd_gqa.restype = i32
+    L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                               i32, vp, vp]
+    L.attn_fwd_fp8.restype = i32
     L.attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -187,6 +190,47 @@ def attn_fwd(q, k, v, *, scale: Optional[float] = None, causal: bool = False,
                                 _seqlens_ptr(seqlens, B, dev), _stream_handle(dev))
         _check(st, "attn_fwd_gqa")
     return (out, lse) if lse is not None else out
+
+
+def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, *, scale: Optional[float] = None,
+                 causal: bool = False, seqlens=None, out_dtype=None, out=None, lse=None):
+    """Attention forward over FP8 E4M3 inputs on the FP8 matrix cores:
+    Q = q8 * q_scale[..., None] (per token), K = k8 * k_scale, V = v8 * v_scale
+    (per batch and K/V head). q8 is [B, H, N, 128], k8 and v8 [B, H_kv, N, 128]
+    (torch.float8_e4m3fn or uint8, the same bytes); q_scale is fp32 [B, H, N],
+    k_scale and v_scale fp32 [B, H_kv]. Returns (O, LSE) with O in out_dtype
+    (torch.bfloat16 by default, or torch.float16) and LSE fp32 [B, H, N]."""
+    import torch
+    B, H, N, d = q8.shape
+    dev = q8.device
+    H_kv = _kv_heads(q8, k8)
+    for name, t, shape in (("q8", q8, (B, H, N, d)), ("k8", k8, (B, H_kv, N, d)),
+                           ("v8", v8, (B, H_kv, N, d))):
+        if t.dtype not in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+            raise TypeError(f"{name} must be float8_e4m3fn or uint8, not {t.dtype}")
+        _check_tensor(name, t, shape, t.dtype, dev)
+    _check_tensor("q_scale", q_scale, (B, H, N), torch.float32, dev)
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _check_tensor(name, t, (B, H_kv), torch.float32, dev)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    if out_dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"out_dtype must be torch.bfloat16 or torch.float16, not {out_dtype}")
+    code = DTYPE_F16 if out_dtype == torch.float16 else DTYPE_BF16
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
+    _check_tensor("out", out, (B, H, N, d), out_dtype, dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _check_tensor("lse", lse, (B, H, N), torch.float32, dev)
+    st = lib().attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
+                            k_scale.data_ptr(), v_scale.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, H, H_kv, N, d, code, float(scale), int(bool(causal)),
+                            _seqlens_ptr(seqlens, B, dev), _stream_handle(dev))
+    _check(st, "attn_fwd_fp8")
+    return out, lse
 
 
 def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int, dtype_code: int = DTYPE_BF16) -> int:

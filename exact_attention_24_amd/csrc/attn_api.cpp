@@ -187,6 +187,41 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   return attn_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, dtype, scale, causal, seqlens, stream);
 }
 
+attn_status attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                         const float* q_scale, const float* k_scale, const float* v_scale,
+                         void* o, float* lse, int B, int H, int H_kv, int N, int d,
+                         attn_dtype out_dtype, float scale, int causal, const int32_t* seqlens,
+                         attn_stream_t stream) {
+  if (out_dtype != ATTN_DTYPE_BF16 && out_dtype != ATTN_DTYPE_F16) {
+    if (out_dtype == ATTN_DTYPE_F32) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_ERR_INVALID_ARG;
+  }
+  attn_status st = check_sizes(B, H, N, d, out_dtype);
+  if (st != ATTN_OK) return st;
+  if (d != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((st = check_heads(H, H_kv)) != ATTN_OK) return st;
+  if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16))
+    return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return ATTN_ERR_INVALID_ARG;
+  if ((lse && !aligned(lse, 4)) || (seqlens && !aligned(seqlens, 4))) return ATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+
+  attn::Fwd8Args a;
+  a.q = q8; a.k = k8; a.v = v8;
+  a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.o = o; a.lse = lse; a.seqlens = seqlens;
+  a.B = B; a.H = H; a.N = N; a.H_kv = H_kv;
+  a.scale = scale;
+  hipError_t e = attn::launch_fwd_fp8(a, causal != 0, out_dtype == ATTN_DTYPE_F16, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    record_hip_error(e, "attn_fwd_fp8 launch");
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype dtype) {
   if (check_sizes(B, H, N, d, dtype) != ATTN_OK) return 0;
   // delta and log2-scaled LSE, one fp32 per row each, each section 256-byte aligned

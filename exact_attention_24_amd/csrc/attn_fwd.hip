@@ -67,22 +67,6 @@ namespace {
 // ----------------------------------------------------------------------------
 constexpr float kLazyRescaleW = 256.0f;  // largest unnormalised weight kept without rescaling
 
-// The batch index of the sequence at position `rank` in the order of
-// decreasing length (ties: lower index first), for B <= 64: lane j holds
-// sequence j's length and counts the sequences ahead of it. Same result in
-// every lane and wave.
-__device__ __forceinline__ int batch_of_rank(const int32_t* seqlens, int B, int N, int rank) {
-  const int lane = threadIdx.x & 63;
-  const int len = lane < B ? min(max(seqlens[lane], 0), N) : -1;
-  int ahead = 0;
-  for (int j = 0; j < B; ++j) {
-    const int lj = __builtin_amdgcn_readlane(len, j);
-    ahead += (lj > len) | ((lj == len) & (j < lane));
-  }
-  const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < B && ahead == rank);
-  return __builtin_ffsll((long long)hit) - 1;
-}
-
 template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void fwd_16_body(const FwdArgs& a) {
   constexpr int BM = 128, BN = 64;

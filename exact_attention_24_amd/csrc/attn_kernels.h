@@ -40,6 +40,23 @@ struct BwdArgs {
   float scale_log2;
 };
 
+// FP8 forward: q, k, v are E4M3 bytes [B,H,N,128] / [B,H_kv,N,128]; scores
+// scale by scale * q_scale[b,h,i] * k_scale[b,hkv], O by v_scale[b,hkv].
+struct Fwd8Args {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* q_scale;     // [B,H,N]
+  const float* k_scale;     // [B,H_kv]
+  const float* v_scale;     // [B,H_kv]
+  void* o;                  // [B,H,N,128] bf16 or fp16
+  float* lse;               // may be null
+  const int32_t* seqlens;   // may be null
+  int B, H, N;
+  int H_kv;
+  float scale;
+};
+
 // Split-KV decode: q, o [B,H,Nq,D], k, v [B,H_kv,Nk,D], split kernel partials
 // in the workspace, merged into o and lse.
 struct DecArgs {
@@ -69,6 +86,7 @@ inline int decode_waves(int col_groups) { return col_groups % 2 == 0 ? 2 : 1; }
 // 16-bit formats: bf16, or fp16 when f16 is set.
 hipError_t launch_fwd_16(const FwdArgs& a, int d, bool causal, bool f16, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fwd8Args& a, bool causal, bool f16_out, hipStream_t stream);
 hipError_t launch_bwd_16(const BwdArgs& a, int d, bool causal, bool f16, hipStream_t stream);
 hipError_t launch_decode_16(const DecArgs& a, int d, bool f16, hipStream_t stream);
 

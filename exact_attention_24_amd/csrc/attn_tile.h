@@ -38,11 +38,17 @@ __device__ __forceinline__ int tile_off(int r, int chunk) {
 //    consecutive chunks per half-wave: chunk c of row r at c ^ (2 * (r % 8)),
 //    or c ^ (2 * ((r / 2) % 4)) for 64 columns; conflict-free for those reads
 //    and, as measured in the backward kernels, for the b128 pattern above too.
-enum TileLayout { TILE_SWZ = 0, TILE_K16 = 1, TILE_T16 = 2 };
+//  - TILE_V8, for 128-byte rows of 8-bit values read by ds_read_b64_tr_b8
+//    with each half-wave addressing the 16 rows r0 + {0..7, 16..23} (r0 a
+//    multiple of 8) at one 16-byte chunk: chunk c of row r at
+//    c ^ (((r / 2) % 4) | 4 * ((r / 16) % 2)), which puts the eight even and
+//    the eight odd rows of that set on eight distinct chunks each.
+enum TileLayout { TILE_SWZ = 0, TILE_K16 = 1, TILE_T16 = 2, TILE_V8 = 3 };
 template <int D, int LAYOUT>
 __device__ __forceinline__ int layout_swz(int r) {
   if constexpr (LAYOUT == TILE_K16) return D == 128 ? (r & 15) : ((r >> 1) & 7);
   else if constexpr (LAYOUT == TILE_T16) return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+  else if constexpr (LAYOUT == TILE_V8) return ((r >> 1) & 3) | ((r >> 2) & 4);
   else return swz<D>(r);
 }
 // Byte offset of element column `col` (a multiple of 4) of row r.
@@ -105,6 +111,7 @@ __device__ __forceinline__ e16x8 pack8(const f32x16& s, int h) {
 template <int D, int ROWS, int NWAVES, int LAYOUT = TILE_SWZ>
 struct TileDma {
   static_assert(LAYOUT == TILE_SWZ || D == 128 || D == 64, "16x16 layouts: 64 or 128 columns");
+  static_assert(LAYOUT != TILE_V8 || D == 64, "TILE_V8: 128-byte rows");
   static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int RPG = 64 / CPR;   // rows per 1 KB wave load
   static constexpr int ITER = ROWS / RPG / NWAVES;

@@ -120,6 +120,38 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
                          int causal, const int32_t* seqlens, attn_stream_t stream);
 
 /*
+ * attn_fwd_fp8 - attention forward over FP8 inputs, both products on the FP8
+ * matrix cores ("FlashAttention：从 Safe Softmax 到分块计算" §9.2: an FP8 path
+ * handles scaling, accumulation and error control; "Attention 算子优化..."
+ * §六: softmax and accumulation stay in fp32).
+ *
+ *  q8        [B,H,N,d] bytes, OCP FP8 E4M3 (as for attn_decode_fp8kv), read only.
+ *  k8, v8    [B,H_kv,N,d] bytes, E4M3, read only; H_kv divides H as for
+ *            attn_fwd_gqa.
+ *  q_scale   [B,H,N] fp32 per-token scales, k_scale and v_scale [B,H_kv] fp32
+ *            per-head scales: the inputs are Q_i = q8_i * q_scale_i,
+ *            K = k8 * k_scale, V = v8 * v_scale, and the result is attn_fwd_gqa
+ *            of those values. Scales must be finite and > 0 (the kernel
+ *            takes the row max of the unscaled scores).
+ *  o         [B,H,N,d] in out_dtype (ATTN_DTYPE_BF16 or ATTN_DTYPE_F16;
+ *            ATTN_DTYPE_F32 gives ATTN_ERR_UNSUPPORTED).
+ *  lse, B, H, N, scale, causal, seqlens, stream: as for attn_fwd.
+ *  d         128 (ATTN_ERR_UNSUPPORTED otherwise).
+ * Precision: the scores are exact products of E4M3 values summed in fp32 on
+ * the matrix cores; the LSE uses the fp32 weights (as attn_fwd). For the V
+ * product each unnormalised weight w (<= 2^8) is rounded to E4M3 (nearest
+ * even): error <= 2^-4 w for w >= 2^-6, <= 2^-10 below. So
+ * |O_i - O_exact_i| <= v_scale * sum_j err_ij |v8_j| / l_i, plus the rounding
+ * of O to out_dtype, where l_i is the row's sum of weights measured against a
+ * reference no larger than the row max (so l_i >= 1).
+ */
+attn_status attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                         const float* q_scale, const float* k_scale, const float* v_scale,
+                         void* o, float* lse, int B, int H, int H_kv, int N, int d,
+                         attn_dtype out_dtype, float scale, int causal, const int32_t* seqlens,
+                         attn_stream_t stream);
+
+/*
  * attn_bwd_workspace_bytes - device workspace that attn_bwd needs for these sizes
  * (it holds -D_i = -rowsum(dO_i o O_i) and LSE_i * log2(e), fp32 [B,H,N] each).
  * Returns 0 for invalid sizes.

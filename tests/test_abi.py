@@ -183,6 +183,26 @@ def test_decode_fp8kv_specific_rules(L):
     assert dec(L, True, vs=P + 2) == INVALID
 
 
+def fwd8(L, q=P, k=P, v=P, qs=P, ks=P, vs=P, o=P, lse=P, B=1, H=2, H_kv=1, N=64, d=128,
+         dtype=1, scale=0.088, causal=0, seqlens=0):
+    return L.attn_fwd_fp8(q, k, v, qs, ks, vs, o, lse, B, H, H_kv, N, d, dtype, scale, causal,
+                          seqlens, 0)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=0), INVALID), (dict(k=0), INVALID), (dict(v=0), INVALID), (dict(o=0), INVALID),
+    (dict(qs=0), INVALID), (dict(ks=0), INVALID), (dict(vs=0), INVALID),
+    (dict(q=P + 8), INVALID), (dict(o=P + 4), INVALID), (dict(qs=P + 2), INVALID),
+    (dict(lse=P + 2), INVALID), (dict(seqlens=P + 1), INVALID),
+    (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(H_kv=3), INVALID), (dict(H_kv=0), INVALID),
+    (dict(d=64), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(dtype=0), UNSUPPORTED),
+    (dict(dtype=9), INVALID), (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
+])
+@cpu_only
+def test_fwd_fp8_rejects_bad_arguments(L, kw, want):
+    assert fwd8(L, **kw) == want
+
+
 def test_decode_workspace_bytes(L):
     # One split: fp32 O [rows][1][d] and (m, l) [rows][1][2], each section rounded to 256 B.
     rows = 2 * 8 * 3
