@@ -124,13 +124,14 @@ __device__ __forceinline__ void fwd8_body(const Fwd8Args& a) {
   kdma.load(kst[0], 0);
   vdma.load(vst[0], 0);
 
-  // Q as B operands: query qq[qb], bytes 32g .. 32g + 31 of its row.
+  // Q as B operands: query qq[qb], bytes 16g .. 16g + 15 and 64 + 16g .. +15
+  // of its row (the k assignment the K operands below use).
   i32x8 qr[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const bool in = qq[qb] < L;
-    const uint8_t* row = Qh + (size_t)qq[qb] * D + 32 * g;
-    qr[qb] = join8(in ? gload16(row) : zero4, in ? gload16(row + 16) : zero4);
+    const uint8_t* row = Qh + (size_t)qq[qb] * D + 16 * g;
+    qr[qb] = join8(in ? gload16(row) : zero4, in ? gload16(row + 64) : zero4);
   }
   // Scores to exp2 arguments: scale * log2(e) * q_scale[query] * k_scale[head].
   // Rows past L (zero Q, output discarded) take q_scale = 1: any positive
@@ -141,15 +142,17 @@ __device__ __forceinline__ void fwd8_body(const Fwd8Args& a) {
   for (int qb = 0; qb < 2; ++qb)
     c2[qb] = a.scale * kLog2e * kv_s * (qq[qb] < L ? a.q_scale[(size_t)bh * N + qq[qb]] : 1.f);
 
-  // K operand: key 16*kb + c16, bytes 32g + 16h .. +15 (h = 0, 1); the row's
-  // swizzle does not depend on kb. V^T operand, read t: source lane (c16, g)
+  // K operand: key 16*kb + c16, 16-byte chunks g and g + 4 of the row (bytes
+  // 16g .. and 64 + 16g ..), so each read touches four consecutive chunks of
+  // 16 rows: conflict-free under TILE_K16 (chunks 2g, 2g + 1 measured four
+  // extra cycles per read); the row's swizzle does not depend on kb. V^T operand, read t: source lane (c16, g)
   // addresses key row 32t + 16*(x/4) + 4g + x%4 (x = c16 / 2) at bytes
   // 16*db + 8*(c16 % 2) .. +7, so the transposing read hands lane (c16, g) the
   // column d = 16*db + c16 of the keys 16*kb + 4g + i (kb = 2t, 2t+1; i < 4):
   // the keys, in the order, that the lane's score accumulators hold.
   uint32_t koff[2], voff[DB];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) koff[h] = (uint32_t)tile_off_lay<64, TILE_K16>(c16, 16 * g + 8 * h);
+  for (int h = 0; h < 2; ++h) koff[h] = (uint32_t)tile_off_lay<64, TILE_K16>(c16, 8 * (g + 4 * h));
   const int x = c16 >> 1;
   const int vrow = 16 * (x >> 2) + 4 * g + (x & 3);
 #pragma unroll
