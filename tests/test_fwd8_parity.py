@@ -178,8 +178,8 @@ def test_fwd8_grouped_heads(causal):
 def test_fwd8_padded_batch(causal):
     """Per-sequence lengths (0, 1, ragged, full) with the padding bytes set to
     0x7F (E4M3 NaN): they are never read, padded O rows are 0 and their LSE
-    -inf."""
-    B, H, N = 4, 2, 400
+    -inf. Eight heads, so the launch takes the longest-sequence-first order."""
+    B, H, N = 4, 8, 400
     lens = torch.tensor([0, 1, 257, 400], dtype=torch.int32)
     c = fp8_case(B, H, N, seed=23 + causal, seqlens=lens)
     for b in range(B):

@@ -95,3 +95,29 @@ def test_decode_graph_replays(fp8):
         ro, rl = call()
         torch.cuda.synchronize()
         assert torch.equal(got[0], ro) and torch.equal(got[1], rl), f"replay {r} differs"
+
+
+def test_fp8_forward_graph_replays():
+    B, H, N, d = 2, 8, 300, 128
+    from attn_inputs import fp8_head
+
+    def draw(seed):
+        y = make_inputs(B, H, N, d, torch.float32, seed=seed)
+        q8, qs = fp8_cache(y["q"])
+        k8, ks = fp8_head(y["k"])
+        v8, vs = fp8_head(y["v"])
+        return [t.to(DEV) for t in (q8, k8, v8, qs, ks, vs)]
+
+    bufs = draw(401)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    g = _capture(lambda: ea.attn_fwd_fp8(*bufs, causal=True, out=o, lse=lse))
+    for r in range(3):
+        for dst, src in zip(bufs, draw(500 + r)):
+            dst.copy_(src)
+        g.replay()
+        torch.cuda.synchronize()
+        got = (o.clone(), lse.clone())
+        ro, rl = ea.attn_fwd_fp8(*bufs, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], ro) and torch.equal(got[1], rl), f"replay {r} differs"
