@@ -10,7 +10,8 @@ Timed region: `--warmup` untimed launches, a device synchronisation, then
 `--steps` launches back to back with one HIP event pair on the launch stream
 around all of them, and a synchronisation. `value` is the region's wall-clock
 rate; `roofline.achieved` divides the FLOPs of one launch by the kernel's
-average launch duration (the event pair's time / steps).
+average launch duration (the event pair's time / steps), and the same object
+gives the fraction of peak at the cold median and cold P90 launch time too.
 
 Distribution pass (the method of the AIInfra FlashAttention note, dpshk.com,
 §3.2: median and P90 of launches timed one by one): the same launches again,
@@ -515,7 +516,10 @@ def main():
                      "traffic": profiled_traffic(),
                      "kernel": "fwd_16_kernel<128, causal, bf16>",
                      "algorithmic": "4*B*H*N^2*d/2 FLOP per launch; duration = HIP event pair "
-                                    "over the timed region / steps"},
+                                    "over the timed region / steps",
+                     "achieved_median_cold": head["tflops_median_cold"],
+                     "frac_median_cold": round(rate(flops, head["ms_median_cold"]) / PEAK_BF16_TFLOPS, 4),
+                     "frac_p90_cold": round(rate(flops, head["ms_p90_cold"]) / PEAK_BF16_TFLOPS, 4)},
     }
     if args.values == "zeros":
         out["data"] = "synthetic, all-zero Q/K/V (power diagnostic, not the benchmark)"
