@@ -26,10 +26,12 @@ DEV = "cuda:0"
 # 4 tokens x group 4 = 16 columns; MQA with 16 heads x 4 tokens = 64 columns
 # (two column blocks, one two-wave workgroup); 16 tokens over 129 keys; MQA
 # with 32 heads x 4 tokens = 128 columns (two two-wave workgroups); 3 tokens x
-# group 32 = 96 columns (three column blocks, one wave each)
+# group 32 = 96 columns (three column blocks, one wave each); 44 heads x 4
+# tokens = 176 columns (six blocks, the last half full: three two-wave
+# workgroups)
 SHAPES = [(2, 8, 2, 1, 300, 128), (1, 4, 4, 5, 700, 64), (3, 32, 8, 4, 1000, 128),
           (1, 16, 1, 4, 333, 128), (2, 2, 2, 16, 129, 64), (1, 32, 1, 4, 500, 128),
-          (2, 64, 2, 3, 260, 64)]
+          (2, 64, 2, 3, 260, 64), (1, 44, 1, 4, 200, 64)]
 
 
 def run_decode(x, scale, causal, kv_lens=None, num_splits=0):
@@ -54,13 +56,14 @@ def test_decode_small(shape, causal, dtype, splits):
     assert_close(lse, rl, LSE_TOL[dn], f"decode{shape} LSE")
 
 
-@pytest.mark.parametrize("heads", [(8, 2), (32, 2)], ids=["one_wave", "two_waves"])
+@pytest.mark.parametrize("heads", [(8, 2), (32, 2), (64, 2)],
+                         ids=["one_wave", "two_waves", "two_workgroups"])
 @pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
 def test_decode_kv_lens(causal, heads):
     """Per-sequence cache lengths: empty, one key, fewer keys than queries (the
     earliest queries then see nothing under the causal mask), ragged, full.
-    With 32 query heads over 2 K/V heads the 64 columns run as a two-wave
-    workgroup."""
+    With 32 query heads over 2 K/V heads the 64 columns run as one two-wave
+    workgroup; with 64 heads, 128 columns, as two."""
     H, H_kv = heads
     B, Nq, Nk, d = 6, 4, 500, 128
     x = make_inputs(B, H, Nk, d, torch.bfloat16, seed=61 + causal, H_kv=H_kv, Nq=Nq)
@@ -180,7 +183,7 @@ def _fp8_case(x):
 # (B, H, H_kv, Nq, Nk, d)
 FP8_SHAPES = [(2, 8, 2, 1, 300, 128), (1, 16, 1, 4, 333, 128), (2, 4, 4, 3, 700, 128),
               (1, 8, 8, 16, 129, 128), (2, 8, 2, 1, 300, 64), (1, 16, 1, 4, 333, 64),
-              (2, 4, 4, 3, 700, 64)]
+              (2, 4, 4, 3, 700, 64), (1, 32, 1, 4, 250, 128)]
 
 
 @pytest.mark.parametrize("splits", [0, 3])
