@@ -23,8 +23,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "draw_seqlens", "workload", "fp8_cache",
-           "fp8_head"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_inputs_device", "draw_seqlens",
+           "workload", "fp8_cache", "fp8_head"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -143,6 +143,31 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: torch.dtype = torch.bfloa
     out["do"] = draw(H, q_rows) if with_grad else None
     out["seqlens"] = (draw_seqlens(gen, B, *seqlen_range)
                       if seqlen_range is not None else None)
+    return out
+
+
+def make_inputs_device(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
+                       device, H_kv: Optional[int] = None, Nq: Optional[int] = None,
+                       with_grad: bool = False) -> dict:
+    """Seeded N(0, 1) Q, K, V (and dO) drawn on ``device`` by a generator of that
+    device, one batch entry at a time, for tensors too large to draw on the host
+    in reasonable time (more than 2^31 elements). Same draw order and shapes as
+    make_inputs; the values are the device generator's, not make_inputs'."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    kv_heads = H if H_kv is None else H_kv
+    q_rows = N if Nq is None else Nq
+
+    def draw(heads: int, rows: int) -> torch.Tensor:
+        out = torch.empty((B, heads, rows, d), dtype=dtype, device=device)
+        for b in range(B):
+            out[b] = torch.randn((heads, rows, d), generator=gen, dtype=torch.float32,
+                                 device=device).to(dtype)
+        return out
+
+    out = {"q": draw(H, q_rows), "k": draw(kv_heads, N), "v": draw(kv_heads, N)}
+    out["do"] = draw(H, q_rows) if with_grad else None
+    out["seqlens"] = None
     return out
 
 

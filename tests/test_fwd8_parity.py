@@ -191,6 +191,23 @@ def test_fwd8_padded_batch(causal):
           f"fp8 fwd padded causal={causal}")
 
 
+def test_fwd8_many_sequences():
+    """More sequences than a wave has lanes (B = 70): the launch takes batch
+    order instead of the longest-sequence-first order; lengths include 0, 1,
+    a tile edge and N, padding bytes set to 0x7F (E4M3 NaN)."""
+    B, H, N = 70, 8, 150
+    g = torch.Generator().manual_seed(29)
+    lens = torch.randint(0, N + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+    lens[:5] = torch.tensor([0, 1, 128, 129, N], dtype=torch.int32)
+    c = fp8_case(B, H, N, seed=29, seqlens=lens)
+    for b in range(B):
+        L = int(lens[b])
+        for name in ("q8", "k8", "v8"):
+            c[name][b, :, L:, :] = 0x7F
+    o, lse = run(c, 1.0 / math.sqrt(128), True, seqlens=lens)
+    check(c, o, lse, 1.0 / math.sqrt(128), True, lens, torch.bfloat16, "fp8 fwd B=70 padded")
+
+
 def test_fwd8_rising_scores_rescale():
     """Scores that rise along the keys (key rows scaled by 1 .. 40 before
     quantisation): later tiles exceed the first tile's reference by far more

@@ -164,6 +164,20 @@ def test_varlen_length_order(causal, heads):
     check_full(x, 1 / math.sqrt(d), causal, "length-ordered varlen")
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
+def test_varlen_many_sequences(causal):
+    """More sequences than a wave has lanes (B = 70): the kernel launches them
+    in batch order instead of by decreasing length; lengths include 0, 1, the
+    tile edges and N; every row checked."""
+    B, H, N, d = 70, 8, 150, 64
+    x = make_inputs(B, H, N, d, torch.bfloat16, seed=83 + causal)
+    g = torch.Generator().manual_seed(83)
+    lens = torch.randint(0, N + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+    lens[:6] = torch.tensor([0, 1, 63, 64, 128, N], dtype=torch.int32)
+    x["seqlens"] = lens
+    check_full(x, 1 / math.sqrt(d), causal, "varlen B=70")
+
+
 # ------------------------------------------------ full workloads, every output
 
 FWD_WORKLOADS = [n for n, w in WORKLOADS.items() if w.Nq is None]  # decode has its own test
