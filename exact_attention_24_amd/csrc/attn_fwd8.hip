@@ -295,23 +295,34 @@ __device__ __forceinline__ void fwd8_body(const Fwd8Args& a) {
   }
 
   // Epilogue: O = v_scale * O_acc / l, rounded to 16 bits; LSE in natural log
-  // units, m * scale * q_scale * k_scale + ln l.
+  // units, m * scale * q_scale * k_scale + ln l. As in the 16-bit forward, each
+  // wave stages its 32 rows in LDS (idle K/V stages, no load in flight) and
+  // stores whole rows, 16-byte pieces, a row per 16 lanes.
+  constexpr int RB = D * 2;                     // bytes per O row (16-bit)
+  constexpr int CPRO = RB / 16;                 // 16-byte chunks per row
+  lds_t* const ost = (wave < 2 ? kst[0] : vst[0]) + (wave & 1) * (32 * RB);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l_tot = sum_quarters(l_part[qb]);
     const int q = qq[qb];
     const bool valid = q < L && l_tot > 0.f;
     const float inv = valid ? v_s / l_tot : 0.f;
-    if (q < N) {
-      e16_t* orow = Oh + (size_t)q * D;
+    const int r = qb * 16 + c16;                // row within the wave's 32
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x2 w = {pack2<F16>(o[db][qb][0] * inv, o[db][qb][1] * inv),
-                         pack2<F16>(o[db][qb][2] * inv, o[db][qb][3] * inv)};
-        gstore8(orow + db * 16 + 4 * g, w);
-      }
-      if (lse_h && g == 0) lse_h[q] = valid ? m_ref[qb] * c2[qb] * kLn2 + logf(l_tot) : -INFINITY;
+    for (int db = 0; db < DB; ++db) {
+      const u32x2 w = {pack2<F16>(o[db][qb][0] * inv, o[db][qb][1] * inv),
+                       pack2<F16>(o[db][qb][2] * inv, o[db][qb][3] * inv)};
+      const int byte = db * 32 + g * 8;         // columns 16 db + 4 g .. +3
+      lds_store8(ost + r * RB + ((((byte >> 4) ^ (r & (CPRO - 1))) << 4) | (byte & 15)), w);
     }
+    if (q < N && lse_h && g == 0) lse_h[q] = valid ? m_ref[qb] * c2[qb] * kLn2 + logf(l_tot) : -INFINITY;
+  }
+  constexpr int RPI = 64 / CPRO;                // rows per store instruction
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int r = it * RPI + lane / CPRO, c = lane % CPRO;
+    const u32x4 w = lds_load16(ost + r * RB + ((c ^ (r & (CPRO - 1))) << 4));
+    if (qw + r < N) gstore16(Oh + (size_t)(qw + r) * D + c * 8, w);
   }
 }
 
