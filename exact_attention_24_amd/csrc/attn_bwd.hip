@@ -72,6 +72,17 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a) {
   }
 }
 
+// Output-row staging for the epilogues: 32 rows of D 16-bit values per wave,
+// 16-byte chunk c of row r at chunk c ^ (r mod chunks-per-row), so that the
+// 8-byte accumulator writes and the 16-byte row reads spread over the banks.
+template <int D>
+struct RowStage {
+  static constexpr int RB = D * 2, CPRO = RB / 16, RPI = 64 / CPRO;
+  __device__ static __forceinline__ uint32_t off(int r, int byte) {
+    return (uint32_t)(r * RB + ((((byte >> 4) ^ (r & (CPRO - 1))) << 4) | (byte & 15)));
+  }
+};
+
 // ---------------------------------------------------------------------------
 // dK, dV: workgroup = 4 waves x 32 keys. Each wave keeps its K and V rows in
 // VGPRs (B operands of S = Q K^T and dP = dO V^T) and accumulates dK^T, dV^T.
@@ -133,6 +144,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
   }
 
   const int kw = n0 + wave * 32;                    // first key of this wave
+  constexpr int RB = RowStage<D>::RB, CPRO = RowStage<D>::CPRO, RPI = RowStage<D>::RPI;
+  auto stage_off = [](int r, int byte) { return RowStage<D>::off(r, byte); };
   const int keys[2] = {kw + c16, kw + 16 + c16};    // this lane's keys (kb = 0, 1)
   const int q_begin = CAUSAL ? (n0 / BM) * BM : 0;
   const int nqt = ((L - q_begin + BM - 1) / BM + 1) & ~1;
@@ -373,21 +386,33 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a) {
     }
   }
 
+  // Each wave stages its 32 dK and dV rows in the idle Q/dO stage buffers
+  // (the last step's barrier has passed, no load is in flight) and stores
+  // whole rows.
+  lds_t* const kst_o = lds_base(wave < 2 ? q0_ : o0_) + (wave & 1) * (32 * RB);
+  lds_t* const vst_o = lds_base(wave < 2 ? q1_ : o1_) + (wave & 1) * (32 * RB);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    if (keys[kb] < N) {
-      const bool kv = keys[kb] < L;
-      e16_t* krow = dKh + (size_t)keys[kb] * D;
-      e16_t* vrow = dVh + (size_t)keys[kb] * D;
+    const bool kv = keys[kb] < L;
+    const int r = kb * 16 + c16;
 #pragma unroll
-      for (int db = 0; db < DBK; ++db) {
-        const u32x2 wk = {kv ? pack2<F16>(dk[db][kb][0] * a.scale, dk[db][kb][1] * a.scale) : 0u,
-                          kv ? pack2<F16>(dk[db][kb][2] * a.scale, dk[db][kb][3] * a.scale) : 0u};
-        const u32x2 wv = {kv ? pack2<F16>(dv[db][kb][0], dv[db][kb][1]) : 0u,
-                          kv ? pack2<F16>(dv[db][kb][2], dv[db][kb][3]) : 0u};
-        gstore8(krow + db * 16 + 4 * g, wk);
-        gstore8(vrow + db * 16 + 4 * g, wv);
-      }
+    for (int db = 0; db < DBK; ++db) {
+      const u32x2 wk = {kv ? pack2<F16>(dk[db][kb][0] * a.scale, dk[db][kb][1] * a.scale) : 0u,
+                        kv ? pack2<F16>(dk[db][kb][2] * a.scale, dk[db][kb][3] * a.scale) : 0u};
+      const u32x2 wv = {kv ? pack2<F16>(dv[db][kb][0], dv[db][kb][1]) : 0u,
+                        kv ? pack2<F16>(dv[db][kb][2], dv[db][kb][3]) : 0u};
+      lds_store8(kst_o + stage_off(r, db * 32 + g * 8), wk);
+      lds_store8(vst_o + stage_off(r, db * 32 + g * 8), wv);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int r = it * RPI + lane / CPRO, c = lane % CPRO;
+    const u32x4 wk = lds_load16(kst_o + stage_off(r, c * 16));
+    const u32x4 wv = lds_load16(vst_o + stage_off(r, c * 16));
+    if (kw + r < N) {
+      gstore16(dKh + (size_t)(kw + r) * D + c * 8, wk);
+      gstore16(dVh + (size_t)(kw + r) * D + c * 8, wv);
     }
   }
 }
