@@ -18,7 +18,7 @@ CSRC = PKG / "csrc"
 LIB_DIR = PKG / "lib"
 LIB_PATH = LIB_DIR / "libattn.so"
 BUILD_DIR = ROOT / "_build"
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd8.hip", "attn_bwd.hip", "attn_decode.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_f32.hip", "attn_fwd8.hip", "attn_bwd.hip", "attn_decode.hip"]
 ARCH = "gfx950"
 
 

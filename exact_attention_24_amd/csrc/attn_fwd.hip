@@ -326,105 +326,6 @@ __global__ void __launch_bounds__(256, 2) fwd_16_kernel(FwdArgs a) {
   fwd_16_body<D, CAUSAL, F16>(a);
 }
 
-// ----------------------------------------------------------------------------
-// fp32 inputs: plain VALU kernel, one query row per lane, 64 rows per
-// workgroup, K/V tiles of 32 keys in LDS (read as broadcasts). Same online
-// softmax; the exponent is formed as (s - m) * scale*log2(e) so its rounding
-// error scales with s - m, which keeps fp32 results within a few ulps.
-// ----------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(64) fwd_f32_kernel(FwdArgs a) {
-  constexpr int BM = 64, BN = 32, C4 = D / 4;
-  __shared__ float4 ks[BN][C4];
-  __shared__ float4 vs[BN][C4];
-  const int lane = threadIdx.x;
-  const int N = a.N;
-  const int nm = (N + BM - 1) / BM;
-  const int bh = blockIdx.x / nm, mt = blockIdx.x % nm;
-  const int b = bh / a.H;
-  int L = N;
-  if (a.seqlens) L = min(max(a.seqlens[b], 0), N);
-  const int m0 = mt * BM, q = m0 + lane;
-  const size_t hoff = (size_t)bh * N * D;
-  const size_t kvoff = (size_t)(b * a.H_kv + (bh % a.H) / (a.H / a.H_kv)) * N * D;
-  const float4* Qh = (const float4*)((const float*)a.q + hoff);
-  const float4* Kh = (const float4*)((const float*)a.k + kvoff);
-  const float4* Vh = (const float4*)((const float*)a.v + kvoff);
-  float4* Oh = (float4*)((float*)a.o + hoff);
-  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-
-  float4 qv[C4], acc[C4];
-#pragma unroll
-  for (int c = 0; c < C4; ++c) {
-    qv[c] = q < L ? Qh[(size_t)q * C4 + c] : z;
-    acc[c] = z;
-  }
-  float m_run = kMaxInit, l_run = 0.f;
-  const float c2 = a.scale_log2;
-  const int kv_end = m0 >= L ? 0 : (CAUSAL ? min(L, m0 + BM) : L);
-  for (int n0 = 0; n0 < kv_end; n0 += BN) {
-    __syncthreads();
-    for (int e = lane; e < BN * C4; e += 64) {
-      const int r = e / C4, c = e % C4, g = n0 + r;
-      ks[r][c] = g < L ? Kh[(size_t)g * C4 + c] : z;
-      vs[r][c] = g < L ? Vh[(size_t)g * C4 + c] : z;
-    }
-    __syncthreads();
-    float s[BN];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < BN; ++j) {
-      float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
-#pragma unroll
-      for (int c = 0; c < C4; ++c) {
-        const float4 kk = ks[j][c];
-        d0 = fmaf(qv[c].x, kk.x, d0);
-        d1 = fmaf(qv[c].y, kk.y, d1);
-        d2 = fmaf(qv[c].z, kk.z, d2);
-        d3 = fmaf(qv[c].w, kk.w, d3);
-      }
-      const int key = n0 + j;
-      s[j] = (key >= L || (CAUSAL && key > q)) ? -INFINITY : (d0 + d1) + (d2 + d3);
-      mx = fmaxf(mx, s[j]);
-    }
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2((m_run - m_new) * c2);
-    float ls = 0.f;
-#pragma unroll
-    for (int j = 0; j < BN; ++j) {
-      s[j] = fast_exp2((s[j] - m_new) * c2);
-      ls += s[j];
-    }
-    l_run = alpha * l_run + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int c = 0; c < C4; ++c) {
-      float4 t = acc[c];
-      t.x *= alpha; t.y *= alpha; t.z *= alpha; t.w *= alpha;
-#pragma unroll
-      for (int j = 0; j < BN; ++j) {
-        const float4 vv = vs[j][c];
-        t.x = fmaf(s[j], vv.x, t.x);
-        t.y = fmaf(s[j], vv.y, t.y);
-        t.z = fmaf(s[j], vv.z, t.z);
-        t.w = fmaf(s[j], vv.w, t.w);
-      }
-      acc[c] = t;
-    }
-  }
-  if (q < N) {
-    const bool valid = q < L && l_run > 0.f;
-    const float inv = valid ? 1.f / l_run : 0.f;
-#pragma unroll
-    for (int c = 0; c < C4; ++c) {
-      float4 t = acc[c];
-      t.x *= inv; t.y *= inv; t.z *= inv; t.w *= inv;
-      Oh[(size_t)q * C4 + c] = t;
-    }
-    if (a.lse) a.lse[(size_t)bh * N + q] = valid ? m_run * a.scale + logf(l_run) : -INFINITY;
-  }
-}
-
 template <int D, bool CAUSAL, bool F16>
 hipError_t launch_16_t(const FwdArgs& a, hipStream_t stream) {
   constexpr int BM = 128;
@@ -441,23 +342,10 @@ hipError_t launch_16_fmt(const FwdArgs& a, int d, bool causal, hipStream_t strea
   return causal ? launch_16_t<128, true, F16>(a, stream) : launch_16_t<128, false, F16>(a, stream);
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_f32_t(const FwdArgs& a, hipStream_t stream) {
-  const int nm = (a.N + 63) / 64;
-  dim3 grid((unsigned)(nm * a.B * a.H)), block(64);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, block, 0, stream, a);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_fwd_16(const FwdArgs& a, int d, bool causal, bool f16, hipStream_t stream) {
   return f16 ? launch_16_fmt<true>(a, d, causal, stream) : launch_16_fmt<false>(a, d, causal, stream);
-}
-
-hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
-  if (d == 64) return causal ? launch_f32_t<64, true>(a, stream) : launch_f32_t<64, false>(a, stream);
-  return causal ? launch_f32_t<128, true>(a, stream) : launch_f32_t<128, false>(a, stream);
 }
 
 }  // namespace attn
