@@ -335,18 +335,29 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
   const int t = threadIdx.x;
   const float* ml = a.part_ml + row * a.splits * 2;
   const float* po = a.part_o + row * a.splits * D + t;
-  // The loads of different splits are independent: unrolled, they are in
-  // flight together instead of one round trip per split.
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < a.splits; ++s) M = ml[2 * s + 1] > 0.f ? fmaxf(M, ml[2 * s]) : M;
-  float l = 0.f, acc = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < a.splits; ++s) {
-    const float ls = ml[2 * s + 1];
-    const float w = ls > 0.f ? fast_exp2(ml[2 * s] - M) : 0.f;
-    l += w * ls;
-    acc += w * po[(size_t)s * D];
+  // One pass with a running max (the merge rule applied split by split), in
+  // blocks of 16 splits whose loads are all issued before any is used (one
+  // memory round trip per block). No branches: the running max starts finite,
+  // and an empty split (l = 0, m = -inf) or a slot past the last split gets
+  // weight exp2(-inf) = 0 and leaves the state unchanged.
+  float M = kMaxInit, l = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < a.splits; s0 += 16) {
+    float ms[16], ls[16], os[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = min(s0 + i, a.splits - 1);
+      ms[i] = s0 + i < a.splits ? ml[2 * s] : -INFINITY;
+      ls[i] = ml[2 * s + 1];
+      os[i] = po[(size_t)s * D];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float Mn = fmaxf(M, ms[i]);
+      const float a0 = fast_exp2(M - Mn), a1 = fast_exp2(ms[i] - Mn);
+      l = l * a0 + ls[i] * a1;
+      acc = acc * a0 + os[i] * a1;
+      M = Mn;
+    }
   }
   const bool valid = l > 0.f;
   const float out = valid ? acc / l : 0.f;
