@@ -56,6 +56,25 @@ def test_decode_small(shape, causal, dtype, splits):
     assert_close(lse, rl, LSE_TOL[dn], f"decode{shape} LSE")
 
 
+@pytest.mark.parametrize("splits", [15, 16, 17, 40], ids=lambda s: f"splits{s}")
+def test_decode_merge_blocks(splits):
+    """The merge takes the splits in blocks of 16 (every load of a block issued
+    before any is used, slots past the last split weighted zero): one block
+    minus one slot, exactly one block, one block plus one split, and three
+    blocks with the last half full, against the oracle. With per-sequence
+    lengths some splits are empty (l = 0) inside a block, and sequence 0 has
+    no keys at all."""
+    B, H, H_kv, Nq, d = 3, 8, 2, 2, 128
+    Nk = 64 * splits  # 64 keys per split, so the plan keeps exactly `splits`
+    x = make_inputs(B, H, Nk, d, torch.bfloat16, seed=67 + splits, H_kv=H_kv, Nq=Nq)
+    lens = torch.tensor([0, Nk // 2 - 5, Nk], dtype=torch.int32)
+    o, lse = run_decode(x, 1 / math.sqrt(d), True, lens, num_splits=splits)
+    ro, rl = oracle.attn_ref_decode(x["q"], x["k"], x["v"], 1 / math.sqrt(d), True, lens)
+    assert_close(o, ro, O_TOL["bf16"], f"decode merge {splits} O")
+    assert_close(lse, rl, LSE_TOL["bf16"], f"decode merge {splits} LSE")
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
 @pytest.mark.parametrize("heads", [(8, 2), (32, 2), (64, 2)],
                          ids=["one_wave", "two_waves", "two_workgroups"])
 @pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
