@@ -30,10 +30,10 @@ namespace {
 // workgroup. K/V tiles of 32 keys: the workgroup loads tile t+1 into
 // registers (all its loads in flight at once) while it computes tile t from
 // LDS; the quad's four lanes read four consecutive chunks of one key row, the
-// other quads the same bytes (a broadcast). Same online softmax as the 16-bit
-// kernels, applied once per tile; the exponent is formed as
-// (s - m) * scale*log2(e) so its rounding error scales with s - m, which keeps
-// fp32 results within a few ulps.
+// other quads the same bytes (a broadcast). The running max moves to the
+// exact max of every tile (no lazy reference as in the 16-bit kernels), and
+// the exponent is formed as (s - m) * scale*log2(e) so its rounding error
+// scales with s - m, which keeps fp32 results within a few ulps.
 // ----------------------------------------------------------------------------
 
 // Sum over the four lanes of a quad; every lane gets the same bits (both
