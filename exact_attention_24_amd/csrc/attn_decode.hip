@@ -337,10 +337,10 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
   const float* po = a.part_o + row * a.splits * D + t;
   // One pass with a running max (the merge rule applied split by split), in
   // blocks of 16 splits whose loads are all issued before any is used (one
-  // memory round trip per block). No branches: the running max starts finite,
-  // and an empty split (l = 0, m = -inf) or a slot past the last split gets
-  // weight exp2(-inf) = 0 and leaves the state unchanged.
-  float M = kMaxInit, l = 0.f, acc = 0.f;
+  // memory round trip per block). No branches: an empty split (l = 0, O = 0,
+  // m = -inf) or a slot past the last split (m taken as -inf) adds nothing,
+  // and a factor whose max did not move is 1 (so -inf - -inf never occurs).
+  float M = -INFINITY, l = 0.f, acc = 0.f;
   for (int s0 = 0; s0 < a.splits; s0 += 16) {
     float ms[16], ls[16], os[16];
 #pragma unroll
@@ -353,7 +353,8 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float Mn = fmaxf(M, ms[i]);
-      const float a0 = fast_exp2(M - Mn), a1 = fast_exp2(ms[i] - Mn);
+      const float a0 = M == Mn ? 1.f : fast_exp2(M - Mn);
+      const float a1 = ms[i] == Mn ? 1.f : fast_exp2(ms[i] - Mn);
       l = l * a0 + ls[i] * a1;
       acc = acc * a0 + os[i] * a1;
       M = Mn;
