@@ -75,6 +75,24 @@ def test_decode_merge_blocks(splits):
     assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
 
 
+def test_decode_merge_very_negative_maxima():
+    """Every score far below -1e30 (a huge scale on negative dot products):
+    each split's running max is about -5.9e33 in log2 units, and the merge
+    must still combine all of them (uniform weights: O is the mean of the
+    visible V rows, LSE = S + ln L)."""
+    B, H, H_kv, Nq, Nk, d = 1, 2, 1, 1, 200, 64
+    x = make_inputs(B, H, Nk, d, torch.bfloat16, seed=71, H_kv=H_kv, Nq=Nq)
+    x["q"] = torch.full_like(x["q"], 8.0)
+    x["k"] = torch.full_like(x["k"], -8.0)
+    scale = 1e30
+    o, lse = run_decode(x, scale, False, num_splits=3)
+    ro, rl = oracle.attn_ref_decode(x["q"], x["k"], x["v"], scale, False)
+    assert torch.all(torch.isfinite(lse))
+    assert_close(o, ro, O_TOL["bf16"], "very negative maxima O")
+    # LSE = -4096e30 + ln 200 in fp32: compare relative to its magnitude
+    assert float(((lse.double() - torch.as_tensor(rl)).abs() / torch.as_tensor(rl).abs()).max()) <= 1e-6
+
+
 @pytest.mark.parametrize("heads", [(8, 2), (32, 2), (64, 2)],
                          ids=["one_wave", "two_waves", "two_workgroups"])
 @pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
