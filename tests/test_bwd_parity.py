@@ -170,24 +170,26 @@ def test_backward_padding_contents_never_read(causal):
 
 def d_rounding_terms(x, scale, causal):
     """How dQ and dK move when D = rowsum(dO o O) is taken over O rounded to
-    bf16, as the method does with the forward's stored output, instead of the
-    exact O: dD_i = sum_c dO_ic (bf16(O_ic) - O_ic), dS moves by -P dD, so dQ
-    by -scale dD_i (P K)_i and dK by -scale P^T (dD o Q); dV does not move.
-    Everything from the oracle (its O rounded here), nothing from the kernel."""
+    the input dtype (bf16 or fp16), as the method does with the forward's
+    stored output, instead of the exact O: dD_i = sum_c dO_ic (r(O_ic) - O_ic),
+    dS moves by -P dD, so dQ by -scale dD_i (P K)_i and dK by
+    -scale P^T (dD o Q); dV does not move. Everything from the oracle (its O
+    rounded here), nothing from the kernel."""
     q, k, v, do = (to_np(x[n]) for n in ("q", "k", "v", "do"))
     eq, ek = np.zeros_like(q), np.zeros_like(k)
     for b in range(q.shape[0]):
         for h in range(q.shape[1]):
             o, _, p = oracle.attn_ref_head(q[b, h], k[b, h], v[b, h], scale, causal, return_p=True)
-            o16 = torch.from_numpy(o).to(torch.bfloat16).double().numpy()
+            o16 = torch.from_numpy(o).to(x["q"].dtype).double().numpy()
             dd = np.sum(do[b, h] * (o16 - o), axis=1)
             eq[b, h] = scale * dd[:, None] * (p @ k[b, h])
             ek[b, h] = scale * (p.T @ (dd[:, None] * q[b, h]))
     return eq, ek, np.zeros_like(eq)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True], ids=["dense", "causal"])
-def test_backward_wide_score_range(causal):
+def test_backward_wide_score_range(causal, dtype):
     """Q and K scaled by 4 (scores over about -80..80: most rows nearly one-hot)
     and, in the last 64 keys, a rising ramp that makes the forward move its
     reference max mid-row: the backward recomputes P from the saved LSE, so any
@@ -197,16 +199,16 @@ def test_backward_wide_score_range(causal):
     that term is derived from the oracle (d_rounding_terms) and added to the
     usual bars."""
     B, H, N, d = 1, 2, 400, 128
-    x = make_inputs(B, H, N, d, torch.bfloat16, seed=37 + causal, with_grad=True)
-    x["q"] = (x["q"].float() * 4).to(torch.bfloat16)
-    x["k"] = (x["k"].float() * 4).to(torch.bfloat16)
-    ramp = torch.linspace(0.0, 6.0, 64).to(torch.bfloat16)
-    x["k"][..., N - 64:, 0] = ramp
-    x["q"][..., 0] = torch.tensor(8.0, dtype=torch.bfloat16)
+    x = make_inputs(B, H, N, d, dtype, seed=37 + causal, with_grad=True)
+    x["q"] = (x["q"].float() * 4).to(dtype)
+    x["k"] = (x["k"].float() * 4).to(dtype)
+    x["k"][..., N - 64:, 0] = torch.linspace(0.0, 6.0, 64).to(dtype)
+    x["q"][..., 0] = torch.tensor(8.0, dtype=dtype)
     scale = 1 / math.sqrt(d)
     got = run_fwd_bwd(x, scale, causal)
     ref = oracle.attn_ref_bwd(x["q"], x["k"], x["v"], x["do"], scale, causal)
-    check_grads(got, ref, f"wide score range causal={causal}", extra=d_rounding_terms(x, scale, causal))
+    check_grads(got, ref, f"wide score range {dtype} causal={causal}",
+                extra=d_rounding_terms(x, scale, causal))
 
 
 def test_backward_deterministic():
