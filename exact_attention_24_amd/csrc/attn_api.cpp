@@ -54,8 +54,9 @@ attn_status check_heads(int H, int H_kv) {
   return ATTN_OK;
 }
 
-// Split plan of the decode: `splits` key ranges of `chunk_keys` keys (a
-// multiple of 32) per (batch, K/V head). 0 requested splits picks enough for
+// Split plan of the decode: `splits` splits per (batch, K/V head), split s
+// taking the 32-key chunks s, s + splits, ... (so each holds about
+// `chunk_keys` keys, a multiple of 32). 0 requested splits picks enough for
 // one resident round of workgroups on 256 CUs (three per CU for the 16-bit
 // split kernel's 48 KiB of LDS, four for the FP8 kernel's 34 KiB). More,
 // shorter workgroups were measured slower (each pays its start-up latency
@@ -332,7 +333,7 @@ attn_status decode_common(const void* q, const void* k, const void* v, const flo
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + decode_part_o_bytes(B, H, Nq, d, p.splits));
   a.B = B; a.H = H; a.H_kv = H_kv; a.Nq = Nq; a.Nk = Nk;
-  a.splits = p.splits; a.chunk_keys = p.chunk_keys; a.col_groups = p.col_groups;
+  a.splits = p.splits; a.col_groups = p.col_groups;
   a.causal = causal != 0;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;

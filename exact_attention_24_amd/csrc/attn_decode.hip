@@ -8,11 +8,15 @@
 // Decode reads the whole K/V cache for very little arithmetic, so it is bound
 // by HBM bandwidth, not by the matrix cores ([OpOpt] §五). With one query row
 // per (batch, head) a forward-style launch would have B*H workgroups each
-// walking the full key range; here the key range of every K/V head is cut
-// into splits that run in parallel ([SafeSoftmax] §10: split the K/V
-// dimension across workgroups), each keeping the online-softmax state
-// (m, l, unnormalised O) of [SafeSoftmax] §3.1 for its keys, and a second
-// kernel combines the splits with the merge rule of [SafeSoftmax] §3.2.
+// walking the full key range; here the keys of every K/V head are dealt to
+// splits that run in parallel ([SafeSoftmax] §10: split the K/V dimension
+// across workgroups), each keeping the online-softmax state (m, l,
+// unnormalised O) of [SafeSoftmax] §3.1 for its keys, and a second kernel
+// combines the splits with the merge rule of [SafeSoftmax] §3.2 (which does
+// not depend on which keys a split holds). Split s of S takes the 32-key
+// chunks s, s + S, s + 2S, ...: the splits of one head then read neighbouring
+// chunks at the same time, which streams from HBM faster than S separate
+// contiguous ranges (measured 3-4% on the eight-token and FP8 workloads).
 //
 // Split kernel: one wave per 32-column block. The G = H / H_kv query heads
 // that share a K/V head ([OpOpt] §五) and their N_q queries are packed into
@@ -132,9 +136,11 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   const size_t qrow = ((size_t)(b * a.H + h) * a.Nq + qi);  // row of q, o, lse, partials
   const int pos = L - a.Nq + qi;                           // this query's position
 
-  const int j_begin = s * a.chunk_keys;
-  const int j_end = min(j_begin + a.chunk_keys, L);
-  const int nch = j_end > j_begin ? (j_end - j_begin + BN - 1) / BN : 0;
+  const int j_begin = s * BN;                  // first key of this split's first chunk
+  const int CS = a.splits * BN;                 // keys between this split's chunks
+  const int nchunks = (L + BN - 1) / BN;
+  const int nch = nchunks > s ? (nchunks - s + a.splits - 1) / a.splits : 0;
+  const int j_end = L;
 
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   e16x8 qr[DS];
@@ -159,7 +165,7 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   };
 #pragma unroll
   for (int c = 0; c < NST - 1; ++c)
-    if (c < nch) load_chunk(c, j_begin + c * BN);
+    if (c < nch) load_chunk(c, j_begin + c * CS);
 
   f32x16 o[DB];
 #pragma unroll
@@ -172,14 +178,14 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
   const int last = a.causal ? min(pos, L - 1) : L - 1;
 
   auto chunk = [&](int t, const int st) {
-    const int j0 = j_begin + t * BN;
+    const int j0 = j_begin + t * CS;
     // Chunk t + NST - 1 goes into the stage chunk t - 1 used; chunk t is
     // waited for (the loads of a wave complete in issue order, so "all but the
     // newest n"). One wave: issue first, then wait. Several: wait for this
     // wave's share of chunk t, meet at the barrier (every share has landed and
     // every wave is done with chunk t - 1), then issue.
     const bool more = t + NST - 1 < nch;
-    if (NW == 1 && more) load_chunk((st + NST - 1) % NST, j0 + (NST - 1) * BN);
+    if (NW == 1 && more) load_chunk((st + NST - 1) % NST, j0 + (NST - 1) * CS);
     const int after = min(NW == 1 ? NST - 1 : NST - 2, nch - 1 - t);  // chunks issued after t
     if (after >= 4) dma_wait_allbut<(NST > 4 ? 4 : 1) * LPC>();
     else if (after == 3) dma_wait_allbut<(NST > 3 ? 3 : 1) * LPC>();
@@ -188,7 +194,7 @@ __device__ __forceinline__ void decode_split_body(const DecArgs& a) {
     else dma_wait();
     if constexpr (NW > 1) {
       __syncthreads();
-      if (more) load_chunk((st + NST - 1) % NST, j0 + (NST - 1) * BN);
+      if (more) load_chunk((st + NST - 1) % NST, j0 + (NST - 1) * CS);
     }
     const lds_t* Kt = kst(st);
     const lds_t* Vt = vst(st);

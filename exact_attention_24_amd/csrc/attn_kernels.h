@@ -71,8 +71,7 @@ struct DecArgs {
   float* part_o;            // workspace: [B*H*Nq][splits][D] unnormalised partial O
   float* part_ml;           // workspace: [B*H*Nq][splits][2] = (m * scale * log2 e, l)
   int B, H, H_kv, Nq, Nk;
-  int splits;               // key-range splits per (batch, K/V head)
-  int chunk_keys;           // keys per split, a multiple of 32
+  int splits;               // splits per (batch, K/V head); split s takes the 32-key chunks s, s + splits, ...
   int col_groups;           // ceil((H / H_kv) * Nq / 32) query-column blocks
   int causal;
   float scale, scale_log2;

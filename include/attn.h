@@ -253,7 +253,8 @@ size_t attn_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d
  *            L_b - Nq .. L_b - 1; with causal != 0 query i sees keys
  *            j <= L_b - Nq + i (with Nq = L_b: the mask of attn_fwd), otherwise
  *            every valid key. A query that sees no key gets O = 0, LSE = -inf.
- *  num_splits  key-range splits per (batch, K/V head); 0 picks a count
+ *  num_splits  splits of the keys per (batch, K/V head), split s of S
+ *            taking the 32-key chunks s, s + S, s + 2S, ...; 0 picks a count
  *            that gives about 512 workgroups for one-wave workgroups over a
  *            16-bit cache, about 768 for query columns in pairs of 32-column
  *            blocks (two-wave workgroups) and about 1024 over an FP8 cache.
