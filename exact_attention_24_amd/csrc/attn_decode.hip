@@ -24,8 +24,8 @@
 // byte is read from HBM once for all of them; two blocks of the same (batch,
 // K/V head, split) run as the two waves of one workgroup and share every
 // chunk load. K/V chunks of 32 keys stream through a ring in LDS by direct
-// buffer->LDS loads (three stages, two chunks in flight; FP8: five stages,
-// four in flight, the same bytes); S^T = K Q^T and O^T += V^T P^T run on
+// buffer->LDS loads (three stages, two chunks in flight; FP8: four stages,
+// three in flight, fewer bytes); S^T = K Q^T and O^T += V^T P^T run on
 // v_mfma_f32_32x32x16 exactly as in the forward kernel.
 //
 // FP8 K/V cache ([OpOpt] §六): K and V stored as OCP E4M3 bytes with one fp32
